@@ -1,0 +1,170 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) fused-attention library.
+ *
+ * What the library computes (the definition every entry point reaches, up to
+ * floating-point rounding order):
+ *
+ *   For batch b, query head h, query row i, with kv head g = floor(h * Hkv / Hq):
+ *     J_i  = { j : 0 <= j < Skv, and (causal == 0 or j <= i + Skv - Sq) }
+ *     s_ij = scale * sum_c q[b,h,i,c] * k[b,g,j,c]
+ *     o[b,h,i,:] = sum_{j in J_i} softmax_j(s_i.) * v[b,g,j,:]
+ *
+ * Sources (the five web pages on small-batch fused attention):
+ *   - "Real-time inference optimisation" (llmapi-app.pages.dev), section
+ *     "Flash Attention optimisation": the tiled kernel with a running max m,
+ *     running sum l and rescaled accumulator, normalised by l at the end.
+ *   - "FlashRT-HF-kernels" (zingnex.cn), section "attention optimisation":
+ *     FlashAttention-style tiling, online softmax, causal-mask optimisation for
+ *     autoregressive generation, MQA/GQA; "Paged Attention" in the operator list.
+ *   - "TensorRT support for FlashAttention" (yongjin360.com): the plugin's
+ *     enqueue launches one kernel on Q, K, V, O with heads, seq_len_q,
+ *     seq_len_kv, head_dim and a stream; it must answer shape/format queries or
+ *     inference fails (hence the explicit status codes below).
+ *   - "FasterTransformer source review" (pptc.cn), sections 1.1 and 3.1:
+ *     context (prefill) is compute-bound, generation (decode) is memory-bound;
+ *     section 2.3: the KV cache is preallocated and owned by the caller.
+ *
+ * Readings where the pages are silent (stated once here, used throughout):
+ *   - causal alignment is bottom-right: query row i sits at absolute position
+ *     Skv - Sq + i (equals top-left when Sq == Skv); causal with Sq > Skv is
+ *     rejected with FA_ERR_SHAPE;
+ *   - consecutive query heads share a kv head (g = floor(h * Hkv / Hq));
+ *   - a row with no visible key (decode with seqlen 0) has output 0;
+ *   - outputs have the dtype of q; bf16 rounding is round-to-nearest-even;
+ *     all accumulation is fp32.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, contiguous row-major, and must be
+ *     16-byte aligned (FA_ERR_ALIGN otherwise).
+ *   - Every buffer is owned by the caller. The library never allocates, frees,
+ *     copies or synchronises; it only enqueues kernels on `stream`
+ *     (a hipStream_t; NULL means the default stream), so every call is safe to
+ *     capture into a HIP graph.
+ *   - Arguments are validated on the host before any launch; a failure returns
+ *     its code and enqueues nothing. Device-resident integers (seqlens,
+ *     block_table) are not read on the host; kernels clamp seqlens to
+ *     [0, max_kv_len].
+ *   - A launch error returns FA_ERR_HIP. Faults inside a kernel surface, as with
+ *     any HIP work, at the caller's next synchronisation.
+ *   - The library keeps no mutable global state and is re-entrant; calls on
+ *     different streams that share a workspace race.
+ */
+#ifndef FA_MI355X_FA_H
+#define FA_MI355X_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  FA_ERR_SHAPE = 2,       /* a size is <= 0, Hq % Hkv != 0, causal with Sq > Skv */
+  FA_ERR_UNSUPPORTED = 3, /* head_dim or page size the kernels do not provide    */
+  FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned             */
+  FA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required             */
+  FA_ERR_HIP = 6,         /* the HIP runtime rejected a launch                   */
+  FA_ERR_ARG = 7          /* scale not finite, tokens_per_split invalid, ...     */
+} fa_status;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* fa_status_string(fa_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+/*
+ * fa_prefill - causal or non-causal MQA/GQA attention over bf16 tensors
+ * (the fused tiled kernel of the "Flash Attention optimisation" section of the
+ * real-time inference page, with the causal mask and head sharing of the
+ * FlashRT-HF-kernels page).
+ *
+ *   q, o : bf16 [B, Hq,  Sq,  d]     k, v : bf16 [B, Hkv, Skv, d]
+ *   d    : 64 or 128 (FA_ERR_UNSUPPORTED otherwise)
+ *   scale: multiplier of q.k (normally 1/sqrt(d)); must be finite
+ *   causal: 0 or 1; bottom-right aligned (see above)
+ *
+ * QK^T and PV run on bf16 MFMA with fp32 accumulation; the probabilities are
+ * rounded to bf16 before the PV product; o is rounded to bf16 (RNE).
+ * o must not alias q, k or v.
+ */
+fa_status fa_prefill(const void* q, const void* k, const void* v, void* o,
+                     int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                     float scale, int causal, void* stream);
+
+/*
+ * fa_prefill_f32 - the same operation with fp32 q, k, v, o and fp32 arithmetic
+ * throughout (no bf16 rounding anywhere). Same arguments and layouts as
+ * fa_prefill; d is 64 or 128.
+ */
+fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
+                         int B, int Hq, int Hkv, int Sq, int Skv, int d,
+                         float scale, int causal, void* stream);
+
+/*
+ * fa_decode_workspace_bytes - bytes of device workspace fa_decode needs:
+ * fp32 partial outputs [B, Hq, n_split, d] and partial log-sum-exps
+ * [B, Hq, n_split], n_split = ceil(max_kv_len / tokens_per_split).
+ * tokens_per_split == 0 selects the default (512). Returns 0 for invalid sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int max_kv_len, int tokens_per_split);
+
+/*
+ * fa_decode - one query token per sequence attending to all of its cached
+ * keys (the paged attention of the FlashRT-HF-kernels operator list and of the
+ * real-time inference page's paged sketch, with the page combination done by a
+ * log-sum-exp merge instead of the sketch's plain sum, which is wrong).
+ *
+ *   q, o        : bf16 [B, Hq, d]
+ *   block_table : NULL  -> contiguous cache, kcache/vcache bf16 [B, max_kv_len, Hkv, d]
+ *                 !NULL -> paged cache, kcache/vcache bf16 [num_pages, 16, Hkv, d];
+ *                          block_table int32 [B, ceil(max_kv_len/16)], entry
+ *                          [b][p] is the physical page of tokens 16p..16p+15 of
+ *                          sequence b; entries p >= ceil(seqlens[b]/16) are never
+ *                          read; page indices must be in range (not checked).
+ *   seqlens     : int32 [B] device array, tokens cached for each sequence,
+ *                 clamped to [0, max_kv_len]; length 0 gives o = 0.
+ *   page_size   : must be 16 when block_table != NULL (ignored otherwise).
+ *   tokens_per_split : KV tokens per split work-group; 0 -> 512; otherwise a
+ *                 positive multiple of 32.
+ *   workspace   : device scratch of at least fa_decode_workspace_bytes(...)
+ *                 bytes, 16-byte aligned; contents undefined after the call.
+ *   d           : 64 or 128.  Hq / Hkv query heads share one kv head.
+ *
+ * Two kernels run in stream order: a split-KV kernel writing per-split
+ * (normalised output, log-sum-exp), then the log-sum-exp merge into o.
+ * For the same tokens_per_split the paged and contiguous paths perform the
+ * same arithmetic in the same order, so their results are bitwise equal.
+ */
+fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
+                    const int32_t* block_table, const int32_t* seqlens, void* o,
+                    int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
+                    int tokens_per_split, float scale,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_merge_lse - combine R rows of S partial attention results by
+ * log-sum-exp (the merge step that replaces the per-page sum of the paged
+ * sketch on the real-time inference page):
+ *   M = max_s lse[r,s];  w_s = exp(lse[r,s] - M)
+ *   o[r,:] = sum_s w_s * o_parts[r,s,:] / sum_s w_s;  lse_out[r] = M + ln(sum_s w_s)
+ * Splits with lse = -inf are empty and are skipped (their o_parts are never
+ * read); a row whose splits are all empty gets o = 0 and lse_out = -inf.
+ *
+ *   o_parts : fp32 [R, S, d] (each part already normalised by its own sum)
+ *   lse     : fp32 [R, S] natural-log log-sum-exp of each part's scores
+ *   o       : [R, d], bf16 when out_bf16 != 0, else fp32
+ *   lse_out : fp32 [R] or NULL
+ *   d       : 64 or 128
+ */
+fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* lse_out,
+                       int R, int S, int d, int out_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_FA_H */

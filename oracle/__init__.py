@@ -1,0 +1,147 @@
+"""fp64 CPU oracle for fused attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The product path (the HIP library and its
+Python binding) never imports, links or runs it, and this package imports
+nothing from the product.
+
+``attention``, ``decode`` and ``merge`` call the plain C implementation in
+``fa_oracle.c`` (the softmax-attention definition written out in fp64; the
+header of that file lists the readings it takes); ``brute`` holds an
+independent pure-Python formulation for tiny shapes.
+
+Page citations: the definition is the one the tiled kernel of the "Real-time
+inference optimisation" page (section "Flash Attention optimisation") reaches
+in exact arithmetic; paged decode follows that page's paged-attention sketch
+(page size 16) with its per-page sum replaced by the log-sum-exp merge.
+
+Every function takes an optional ``lib`` path so that the pin suite can also be
+run against deliberately broken copies of the C source (mutation testing).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(_HERE, "fa_oracle.c")
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_libs: dict = {}
+
+
+def build(force: bool = True, src: str = SRC, out: str = LIB_PATH) -> str:
+    """Compile an oracle C source into a shared library with gcc (OpenMP, no fast-math)."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall", "-o", tmp, src, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _load(path: str | None = None):
+    if path is None:
+        path = LIB_PATH
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(SRC):
+            build(force=True)
+    lib = _libs.get(path)
+    if lib is None:
+        lib = ctypes.CDLL(path)
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        ci = ctypes.c_int
+        lib.oracle_attention_f64.argtypes = [dp, dp, dp, dp, dp, ci, ci, ci, ci, ci, ci, ctypes.c_double, ci]
+        lib.oracle_attention_f64.restype = ci
+        lib.oracle_decode_f64.argtypes = [dp, dp, dp, ip, ci, ip, dp, dp, ci, ci, ci, ci, ci, ci, ctypes.c_double]
+        lib.oracle_decode_f64.restype = ci
+        lib.oracle_merge_f64.argtypes = [dp, dp, dp, dp, ci, ci, ci]
+        lib.oracle_merge_f64.restype = ci
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ci
+        _libs[path] = lib
+    return lib
+
+
+def _dptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _iptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def num_threads(lib: str | None = None) -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all visible cores)."""
+    return int(_load(lib).oracle_num_threads())
+
+
+def attention(q, k, v, scale: float, causal: bool, lib: str | None = None):
+    """Plain softmax attention in fp64.
+
+    q: [B, Hq, Sq, d]; k, v: [B, Hkv, Skv, d] (any real dtype, converted exactly
+    to float64). Returns (o [B, Hq, Sq, d], lse [B, Hq, Sq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Sq, d = q.shape
+    Bk, Hkv, Skv, dk = k.shape
+    assert Bk == B and dk == d and v.shape == k.shape
+    o = np.empty((B, Hq, Sq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, Sq), dtype=np.float64)
+    rc = _load(lib).oracle_attention_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse),
+                                         B, Hq, Hkv, Sq, Skv, d, float(scale), int(bool(causal)))
+    if rc != 0:
+        raise ValueError("oracle_attention_f64: invalid shape")
+    return o, lse
+
+
+def decode(q, kcache, vcache, seqlens, scale: float, block_table=None, page_size: int = 16, max_kv_len=None,
+           lib: str | None = None):
+    """Single-query attention over each sequence's cached tokens, in fp64.
+
+    q: [B, Hq, d]. Contiguous cache (block_table None): kcache, vcache
+    [B, max_kv_len, Hkv, d]. Paged cache: [num_pages, page_size, Hkv, d] with
+    block_table int32 [B, pages_per_seq]. seqlens int32 [B].
+    Returns (o [B, Hq, d], lse [B, Hq]).
+    """
+    q, kc, vc = _f64(q), _f64(kcache), _f64(vcache)
+    B, Hq, d = q.shape
+    Hkv = kc.shape[2]
+    seqlens = np.ascontiguousarray(seqlens, dtype=np.int32)
+    if block_table is None:
+        mkl = kc.shape[1] if max_kv_len is None else int(max_kv_len)
+        bt, pps, page = None, 0, 1
+    else:
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        pps = bt.shape[1]
+        page = int(page_size)
+        mkl = pps * page if max_kv_len is None else int(max_kv_len)
+    o = np.empty((B, Hq, d), dtype=np.float64)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    rc = _load(lib).oracle_decode_f64(_dptr(q), _dptr(kc), _dptr(vc), _iptr(bt), pps, _iptr(seqlens),
+                                      _dptr(o), _dptr(lse), B, Hq, Hkv, d, mkl, page, float(scale))
+    if rc != 0:
+        raise ValueError("oracle_decode_f64: invalid shape")
+    return o, lse
+
+
+def merge(o_parts, lse_parts, lib: str | None = None):
+    """Log-sum-exp merge. o_parts [R, S, d] (normalised parts), lse_parts [R, S].
+    Returns (o [R, d], lse [R])."""
+    op, lp = _f64(o_parts), _f64(lse_parts)
+    R, S, d = op.shape
+    assert lp.shape == (R, S)
+    o = np.empty((R, d), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    _load(lib).oracle_merge_f64(_dptr(op), _dptr(lp), _dptr(o), _dptr(lse), R, S, d)
+    return o, lse

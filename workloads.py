@@ -1,0 +1,236 @@
+"""Seeded synthetic workloads for the attention kernels and the oracle.
+
+This module only draws and lays out inputs; it holds none of the attention
+arithmetic. Both the GPU path (through the binding) and the fp64 oracle consume
+exactly what it returns: bf16 data is produced as bf16 bit patterns (uint16),
+and the oracle reads the same bits converted exactly to float64.
+
+Generator: numpy's PCG64 seeded with SeedSequence([seed, stream]); normal
+values come from ``Generator.standard_normal`` in float32 and are rounded to
+bf16 with round-to-nearest-even. Streams are numbered so that adding a draw
+never changes an earlier one.
+
+Workloads (shapes from the small-batch inference setting of the pages: 32
+heads of dimension 128 as in the FlashRT-HF-kernels usage example, 32k
+contexts as on the TensorRT page, 256K contexts as on the FlashRT page, page
+size 16 as in the paged sketch of the real-time inference page):
+
+  prefill_f32_b1h1s128d64            fp32 causal, B=1, H=1, Sq=Skv=128, d=64
+  prefill_gqa_b1h32x8s2048d128       bf16 GQA causal, B=1, Hq=32, Hkv=8, Sq=Skv=2048, d=128
+  decode_contig_b4h32x8kv32768d128   bf16 decode, B=4, Hq=32, Hkv=8, 32768 cached tokens each
+  decode_paged_b8h32x8kv1k16kd128    bf16 paged decode, B=8, lengths U{1024..16384}, page 16
+  decode_long_b1h16x2kv256kd128      bf16 paged decode, B=1, Hq=16, Hkv=2, 262144 tokens
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+PAGE = 16
+BF16_NAN = np.uint16(0x7FC0)
+
+
+def rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), int(stream)])))
+
+
+def normal_f32(seed: int, stream: int, shape) -> np.ndarray:
+    return rng(seed, stream).standard_normal(size=shape, dtype=np.float32)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (round-to-nearest-even); returns uint16 bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    r = ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        r[nan] = BF16_NAN
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+def normal_bf16(seed: int, stream: int, shape) -> np.ndarray:
+    return f32_to_bf16_bits(normal_f32(seed, stream, shape))
+
+
+# --------------------------------------------------------------------------- prefill
+
+
+@dataclass
+class PrefillCase:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int
+    d: int
+    causal: bool
+    dtype: str  # "bf16" (uint16 bits) or "f32"
+    scale: float
+    q: np.ndarray = field(repr=False)
+    k: np.ndarray = field(repr=False)
+    v: np.ndarray = field(repr=False)
+
+    def as_f64(self):
+        conv = bf16_bits_to_f64 if self.dtype == "bf16" else (lambda a: a.astype(np.float64))
+        return conv(self.q), conv(self.k), conv(self.v)
+
+
+def prefill_case(B, Hq, Hkv, Sq, Skv, d, causal=True, dtype="bf16", seed=1, scale=None, name=None) -> PrefillCase:
+    """q [B,Hq,Sq,d], k/v [B,Hkv,Skv,d], i.i.d. N(0,1) from (seed, stream 0/1/2)."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    shp_q, shp_kv = (B, Hq, Sq, d), (B, Hkv, Skv, d)
+    if dtype == "bf16":
+        q, k, v = normal_bf16(seed, 0, shp_q), normal_bf16(seed, 1, shp_kv), normal_bf16(seed, 2, shp_kv)
+    elif dtype == "f32":
+        q, k, v = normal_f32(seed, 0, shp_q), normal_f32(seed, 1, shp_kv), normal_f32(seed, 2, shp_kv)
+    else:
+        raise ValueError(dtype)
+    if name is None:
+        name = f"prefill_{dtype}_b{B}h{Hq}x{Hkv}sq{Sq}skv{Skv}d{d}{'_causal' if causal else ''}"
+    return PrefillCase(name, B, Hq, Hkv, Sq, Skv, d, bool(causal), dtype, float(scale), q, k, v)
+
+
+def prefill_f32_small() -> PrefillCase:
+    """fp32 single-head causal forward: B=1, H=1, Sq=Skv=128, d=64, scale 1/8."""
+    return prefill_case(1, 1, 1, 128, 128, 64, True, "f32", seed=1001, scale=1.0 / math.sqrt(64),
+                        name="prefill_f32_b1h1s128d64")
+
+
+def prefill_gqa_2k() -> PrefillCase:
+    """bf16 GQA causal prefill: B=1, Hq=32, Hkv=8, Sq=Skv=2048, d=128, scale 1/sqrt(128)."""
+    return prefill_case(1, 32, 8, 2048, 2048, 128, True, "bf16", seed=1002, scale=1.0 / math.sqrt(128),
+                        name="prefill_gqa_b1h32x8s2048d128")
+
+
+# --------------------------------------------------------------------------- decode
+
+
+@dataclass
+class DecodeCase:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    d: int
+    max_kv_len: int
+    scale: float
+    seqlens: np.ndarray  # int32 [B]
+    q: np.ndarray = field(repr=False)  # bf16 bits [B,Hq,d]
+    kcache: np.ndarray = field(repr=False)  # bf16 bits: [B,max_kv_len,Hkv,d] or pool [P,16,Hkv,d]
+    vcache: np.ndarray = field(repr=False)
+    block_table: np.ndarray | None = field(default=None, repr=False)  # int32 [B, ceil(max_kv_len/16)]
+
+    @property
+    def paged(self) -> bool:
+        return self.block_table is not None
+
+    def total_tokens(self) -> int:
+        return int(np.clip(self.seqlens, 0, self.max_kv_len).sum())
+
+
+def decode_contiguous(B, Hq, Hkv, d, max_kv_len, seqlens=None, seed=7, name=None, poison=False) -> DecodeCase:
+    """Contiguous cache [B, max_kv_len, Hkv, d]; q [B,Hq,d]; N(0,1).
+    seqlens default to max_kv_len. With poison, slots t >= seqlens[b] hold NaN."""
+    q = normal_bf16(seed, 0, (B, Hq, d))
+    kc = normal_bf16(seed, 1, (B, max_kv_len, Hkv, d))
+    vc = normal_bf16(seed, 2, (B, max_kv_len, Hkv, d))
+    if seqlens is None:
+        seqlens = np.full((B,), max_kv_len, dtype=np.int32)
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    if poison:
+        for b in range(B):
+            L = max(0, min(int(seqlens[b]), max_kv_len))
+            kc[b, L:] = BF16_NAN
+            vc[b, L:] = BF16_NAN
+    if name is None:
+        name = f"decode_contig_b{B}h{Hq}x{Hkv}kv{max_kv_len}d{d}"
+    return DecodeCase(name, B, Hq, Hkv, d, int(max_kv_len), 1.0 / math.sqrt(d), seqlens, q, kc, vc, None)
+
+
+def decode_paged(B, Hq, Hkv, d, seqlens, max_kv_len, seed=11, slack_pages=7, name=None, poison=False) -> DecodeCase:
+    """Shared page pool [P, 16, Hkv, d] with P = sum ceil(len_b/16) + slack pages.
+    The pool order is a seeded random permutation: sequence b owns
+    perm[off_b : off_b + ceil(len_b/16)]. Unused block-table entries point at the
+    first slack page. With poison, tail slots past len_b and all slack pages are NaN."""
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    npages = [(int(min(max(L, 0), max_kv_len)) + PAGE - 1) // PAGE for L in seqlens]
+    used = sum(npages)
+    P = used + max(1, slack_pages)
+    perm = rng(seed, 3).permutation(P).astype(np.int32)
+    q = normal_bf16(seed, 0, (B, Hq, d))
+    kp = normal_bf16(seed, 1, (P, PAGE, Hkv, d))
+    vp = normal_bf16(seed, 2, (P, PAGE, Hkv, d))
+    pps = (max_kv_len + PAGE - 1) // PAGE
+    slack0 = int(perm[used])
+    bt = np.full((B, pps), slack0, dtype=np.int32)
+    off = 0
+    for b in range(B):
+        bt[b, : npages[b]] = perm[off : off + npages[b]]
+        off += npages[b]
+    if poison:
+        for s in perm[used:]:
+            kp[s] = BF16_NAN
+            vp[s] = BF16_NAN
+        for b in range(B):
+            L = int(min(max(seqlens[b], 0), max_kv_len))
+            if L % PAGE and npages[b]:
+                last = bt[b, npages[b] - 1]
+                kp[last, L % PAGE :] = BF16_NAN
+                vp[last, L % PAGE :] = BF16_NAN
+    if name is None:
+        name = f"decode_paged_b{B}h{Hq}x{Hkv}d{d}"
+    return DecodeCase(name, B, Hq, Hkv, d, int(max_kv_len), 1.0 / math.sqrt(d), seqlens, q, kp, vp, bt)
+
+
+def decode_contig_32k() -> DecodeCase:
+    """Contiguous decode: B=4, Hq=32, Hkv=8, 32768 cached tokens each, d=128."""
+    return decode_contiguous(4, 32, 8, 128, 32768, seed=1003, name="decode_contig_b4h32x8kv32768d128")
+
+
+def paged_lengths(seed: int, B: int, lo: int, hi: int) -> np.ndarray:
+    """Integer lengths uniform on [lo, hi], both ends inclusive."""
+    return rng(seed, 4).integers(lo, hi + 1, size=B).astype(np.int32)
+
+
+def decode_paged_mixed(poison=False) -> DecodeCase:
+    """Paged decode: B=8, Hq=32, Hkv=8, d=128, lengths U{1024..16384}, page 16, shuffled pool."""
+    lens = paged_lengths(1004, 8, 1024, 16384)
+    return decode_paged(8, 32, 8, 128, lens, 16384, seed=1004, name="decode_paged_b8h32x8kv1k16kd128", poison=poison)
+
+
+def decode_long_256k(poison=False) -> DecodeCase:
+    """Long-context paged decode: B=1, Hq=16, Hkv=2, d=128, 262144 tokens, shuffled pages."""
+    return decode_paged(1, 16, 2, 128, np.array([262144], dtype=np.int32), 262144, seed=1005,
+                        name="decode_long_b1h16x2kv256kd128", poison=poison)
+
+
+def paged_from_contiguous(case: DecodeCase, seed: int = 99) -> DecodeCase:
+    """Scatter a contiguous cache into a shuffled page pool (same values, same
+    lengths): the paged view of exactly the same data."""
+    assert not case.paged and case.max_kv_len % PAGE == 0
+    B, L = case.B, case.max_kv_len
+    pps = L // PAGE
+    P = B * pps
+    perm = rng(seed, 5).permutation(P).astype(np.int32)
+    bt = perm.reshape(B, pps)
+    kp = np.empty((P, PAGE, case.Hkv, case.d), dtype=np.uint16)
+    vp = np.empty_like(kp)
+    kp[bt.reshape(-1)] = case.kcache.reshape(B * pps, PAGE, case.Hkv, case.d)
+    vp[bt.reshape(-1)] = case.vcache.reshape(B * pps, PAGE, case.Hkv, case.d)
+    return DecodeCase(case.name + "_paged", case.B, case.Hq, case.Hkv, case.d, L, case.scale,
+                      case.seqlens.copy(), case.q, kp, vp, bt)
