@@ -1,0 +1,145 @@
+// fa_api.hip - the extern "C" entry points declared in include/fa.h.
+// Validates every argument on the host (no device access, no allocation, no
+// synchronisation), then enqueues the gfx950 kernels on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+constexpr int kDefaultTps = 512;
+constexpr int kMaxTps = 1024;
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+fa_status from_hip(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+fa_status check_prefill(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq,
+                        int Skv, int d, float scale, int causal) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || d <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (B > kMaxGridYZ || Hq > kMaxGridYZ) return FA_ERR_SHAPE;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (causal && Sq > Skv) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+fa::PrefillParams make_prefill(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                               int Sq, int Skv, float scale, int causal) {
+  fa::PrefillParams p;
+  p.q = q; p.k = k; p.v = v; p.o = o;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
+  p.c = fabsf(scale) * fa::kLog2e;
+  p.neg = scale < 0.f ? 1 : 0;
+  p.causal = causal;
+  p.nT = (Sq + 127) / 128;
+  p.nP = (p.nT + 1) / 2;
+  return p;
+}
+
+int resolve_tps(int tps) { return tps == 0 ? kDefaultTps : tps; }
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (<= 0, Hq % Hkv != 0, causal with Sq > Skv, or too large)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim must be 64 or 128 and page_size 16";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
+    case FA_ERR_ARG: return "FA_ERR_ARG: invalid argument (scale not finite, causal not 0/1, bad tokens_per_split)";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+int fa_version(void) { return 100; }
+
+fa_status fa_prefill(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq, int Skv,
+                     int d, float scale, int causal, void* stream) {
+  fa_status st = check_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, scale, causal);
+  if (st != FA_OK) return st;
+  fa::PrefillParams p = make_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, scale, causal);
+  return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+}
+
+fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq,
+                         int Skv, int d, float scale, int causal, void* stream) {
+  fa_status st = check_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, scale, causal);
+  if (st != FA_OK) return st;
+  fa::PrefillParams p = make_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, scale, causal);
+  return from_hip(fa::launch_prefill_f32(p, d, scale, (hipStream_t)stream));
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int d, int max_kv_len, int tokens_per_split) {
+  const int tps = resolve_tps(tokens_per_split);
+  if (B <= 0 || Hq <= 0 || d <= 0 || max_kv_len <= 0 || tps <= 0) return 0;
+  const size_t nsplit = ((size_t)max_kv_len + tps - 1) / tps;
+  const size_t rows = (size_t)B * Hq * nsplit;
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                    const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
+                    int tokens_per_split, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !kcache || !vcache || !seqlens || !o) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_kv_len <= 0) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (block_table && page_size != 16) return FA_ERR_UNSUPPORTED;
+  const int tps = resolve_tps(tokens_per_split);
+  if (tps <= 0 || tps % 32 != 0 || tps > kMaxTps) return FA_ERR_ARG;
+  if (!isfinite(scale)) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o)) return FA_ERR_ALIGN;
+  if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
+  const int G = Hq / Hkv;
+  const int hchunks = (G + 15) / 16;
+  if (B > kMaxGridYZ || (long)Hkv * hchunks > kMaxGridYZ) return FA_ERR_SHAPE;
+  if (!block_table && (size_t)B * (size_t)max_kv_len > (size_t)INT32_MAX) return FA_ERR_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, Hq, d, max_kv_len, tps);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+
+  fa::DecodeParams p;
+  p.q = q; p.kc = kcache; p.vc = vcache; p.bt = block_table; p.lens = seqlens; p.o = o;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.max_len = max_kv_len;
+  p.pages_per_seq = (max_kv_len + 15) / 16;
+  p.tps = tps;
+  p.nsplit = (max_kv_len + tps - 1) / tps;
+  p.G = G;
+  p.hchunks = hchunks;
+  p.c = fabsf(scale) * fa::kLog2e;
+  p.neg = scale < 0.f ? 1 : 0;
+  const size_t rows = (size_t)B * Hq * p.nsplit;
+  p.ws_o = (float*)workspace;
+  p.ws_lse = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
+  return from_hip(fa::launch_decode_bf16(p, d, (hipStream_t)stream));
+}
+
+fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* lse_out, int R, int S, int d,
+                       int out_bf16, void* stream) {
+  if (!o_parts || !lse || !o) return FA_ERR_NULL;
+  if (R <= 0 || S <= 0 || d <= 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!aligned16(o_parts) || !aligned16(o) || !aligned4(lse) || (lse_out && !aligned4(lse_out)))
+    return FA_ERR_ALIGN;
+  fa::MergeParams m;
+  m.o_parts = o_parts; m.lse = lse; m.o = o; m.lse_out = lse_out; m.lens = nullptr;
+  m.R = R; m.S = S; m.Hq = 1; m.tps = 1; m.max_len = 0; m.out_bf16 = out_bf16 ? 1 : 0;
+  return from_hip(fa::launch_merge(m, d, (hipStream_t)stream));
+}
+
+}  // extern "C"

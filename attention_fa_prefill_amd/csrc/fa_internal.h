@@ -1,0 +1,68 @@
+// fa_internal.h - types and launchers shared by the gfx950 kernels and the
+// C-ABI layer. Nothing here is part of the public interface (include/fa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// log2(e): the kernels evaluate exp(x) as exp2(x * log2(e)) with the factor
+// folded into the softmax scale.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------- prefill
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int B, Hq, Hkv, Sq, Skv;
+  float c;     // |scale| * log2(e)
+  int neg;     // scale < 0: q is negated on load (exact) so that c >= 0
+  int causal;  // bottom-right aligned
+  int nT;      // query tiles of 128 rows
+  int nP;      // work-groups per (b, h): pairs of query tiles
+};
+
+hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_prefill_f32(const PrefillParams& p, int d, float scale, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode
+struct DecodeParams {
+  const void* q;       // bf16 [B, Hq, d]
+  const void* kc;      // bf16 rows of [*, Hkv, d]
+  const void* vc;
+  const int32_t* bt;   // block table or nullptr
+  const int32_t* lens; // [B]
+  void* o;             // bf16 [B, Hq, d]
+  float* ws_o;         // fp32 [B, Hq, nsplit, d]
+  float* ws_lse;       // fp32 [B, Hq, nsplit]
+  int B, Hq, Hkv, max_len, pages_per_seq, tps, nsplit;
+  int G;               // query heads per kv head
+  int hchunks;         // ceil(G / 16)
+  float c;             // |scale| * log2(e)
+  int neg;
+};
+
+hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
+
+struct MergeParams {
+  const float* o_parts;  // [R, S, d]
+  const float* lse;      // [R, S] natural log
+  void* o;               // [R, d] bf16 or fp32
+  float* lse_out;        // [R] or nullptr
+  const int32_t* lens;   // if not null: valid splits of row r = ceil(clamp(lens[r / Hq]) / tps)
+  int R, S, Hq, tps, max_len, out_bf16;
+};
+
+hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,120 @@
+"""The C-ABI library loads, exports every symbol include/fa.h declares, and
+rejects invalid calls on the host with the documented status codes.
+
+CPU only: every call below is invalid in exactly one way, so the library
+returns before any launch and no GPU is touched.
+"""
+import os
+import re
+
+import pytest
+
+import attention_fa_prefill_amd as fa
+
+pytestmark = pytest.mark.cpu
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, HIP, ARG = range(8)
+A = 0x10000  # a 16-byte aligned, never dereferenced address
+
+
+def header_symbols():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    return sorted(set(re.findall(r"^\S.*?\b(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fa.lib()
+    declared = header_symbols()
+    assert declared, "no declarations found in include/fa.h"
+    assert set(declared) == set(fa.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    for code, name in fa.STATUS_NAMES.items():
+        assert fa.status_string(code).startswith(name)
+    assert fa.status_string(99) == "FA_ERR_UNKNOWN"
+    assert fa.lib().fa_version() == 100
+
+
+def prefill(fn="fa_prefill", q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, Sq=8, Skv=8, d=128, scale=0.125, causal=1):
+    return getattr(fa.lib(), fn)(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, scale, causal, None)
+
+
+@pytest.mark.parametrize("fn", ["fa_prefill", "fa_prefill_f32"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
+    (dict(B=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=0), SHAPE), (dict(Sq=0), SHAPE), (dict(Skv=-1), SHAPE),
+    (dict(Hq=6, Hkv=4), SHAPE), (dict(Sq=9, Skv=8, causal=1), SHAPE), (dict(B=70000), SHAPE),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(d=0), SHAPE),
+    (dict(scale=float("inf")), ARG), (dict(scale=float("nan")), ARG), (dict(causal=2), ARG),
+    (dict(q=A + 8), ALIGN), (dict(k=A + 4), ALIGN), (dict(v=A + 2), ALIGN), (dict(o=A + 1), ALIGN),
+])
+def test_prefill_rejects(fn, kw, code):
+    assert prefill(fn, **kw) == code
+
+
+def decode(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, page=16, tps=0, scale=0.1,
+           ws=A, wsb=None):
+    if wsb is None:
+        wsb = fa.decode_workspace_bytes(B, Hq, d, L, tps) if B > 0 else 0
+    return fa.lib().fa_decode(q, k, v, bt, lens, o, B, Hq, Hkv, d, L, page, tps, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(lens=None), NULL), (dict(o=None), NULL),
+    (dict(B=0, wsb=1 << 20), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(L=0, wsb=1 << 20), SHAPE),
+    (dict(Hkv=0), SHAPE),
+    (dict(d=80), UNSUP), (dict(bt=A, page=32), UNSUP), (dict(bt=A, page=8), UNSUP),
+    (dict(tps=48), ARG), (dict(tps=-32), ARG), (dict(tps=2048), ARG), (dict(scale=float("nan")), ARG),
+    (dict(q=A + 2), ALIGN), (dict(k=A + 8), ALIGN), (dict(o=A + 4), ALIGN), (dict(lens=A + 2), ALIGN),
+    (dict(bt=A + 1), ALIGN), (dict(ws=A + 8), ALIGN),
+    (dict(ws=None), WS), (dict(wsb=16), WS),
+])
+def test_decode_rejects(kw, code):
+    assert decode(**kw) == code
+
+
+def test_decode_workspace_bytes():
+    # [B, Hq, nsplit, d] fp32 partials + [B, Hq, nsplit] fp32 lse, each rounded up to 256 bytes
+    n = 32768 // 512
+    assert fa.decode_workspace_bytes(4, 32, 128, 32768, 0) == 4 * 32 * n * 128 * 4 + 4 * 32 * n * 4
+    assert fa.decode_workspace_bytes(4, 32, 128, 32768, 512) == fa.decode_workspace_bytes(4, 32, 128, 32768, 0)
+    assert fa.decode_workspace_bytes(1, 1, 64, 1, 32) == 256 + 256
+    assert fa.decode_workspace_bytes(0, 1, 64, 1, 32) == 0
+    n5 = 262144 // 512
+    assert n5 >= 256  # the long-context workload merges at least 256 splits
+    assert fa.decode_workspace_bytes(1, 16, 128, 262144, 0) == 16 * n5 * 128 * 4 + 16 * n5 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(op=None), NULL), (dict(lse=None), NULL), (dict(o=None), NULL),
+    (dict(R=0), SHAPE), (dict(S=0), SHAPE), (dict(d=32), UNSUP),
+    (dict(op=A + 4), ALIGN), (dict(o=A + 8), ALIGN), (dict(lse=A + 2), ALIGN), (dict(lo=A + 1), ALIGN),
+])
+def test_merge_rejects(kw, code):
+    a = dict(op=A, lse=A, o=A, lo=None, R=4, S=3, d=128)
+    a.update(kw)
+    assert fa.lib().fa_merge_lse(a["op"], a["lse"], a["o"], a["lo"], a["R"], a["S"], a["d"], 1, None) == code
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.prefill(q, q, q)
+    with pytest.raises(ValueError):
+        fa.decode(torch.zeros(1, 1, 64, dtype=torch.bfloat16), torch.zeros(1, 16, 1, 64, dtype=torch.bfloat16),
+                  torch.zeros(1, 16, 1, 64, dtype=torch.bfloat16), torch.zeros(1, dtype=torch.int32))
+
+
+def test_product_code_does_not_touch_the_oracle():
+    """The HIP library and its binding never import, link or run oracle/."""
+    pkg = os.path.join(ROOT, "attention_fa_prefill_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text and "liboracle" not in text, f

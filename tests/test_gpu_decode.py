@@ -1,0 +1,180 @@
+"""GPU parity of fa_decode (split-KV + log-sum-exp merge) and fa_merge_lse.
+
+Full-size contiguous, paged and long-context workloads are compared element by
+element with the fp64 oracle; the paged path is checked to reproduce the
+contiguous path bit for bit on the same data; poisoned cache slots (NaN past
+each sequence's length and in unused pages) must not reach the output.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import attention_fa_prefill_amd as fa
+import oracle
+import workloads
+from tests.gpu_util import (assert_bf16_close, dev_bf16, dev_f32, dev_i32, host_bits, host_f64, torch_gpu)
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case, tps=0):
+    torch_gpu()
+    print(f"case {case.name} paged={case.paged} tps={tps}", flush=True)
+    q, kc, vc = dev_bf16(case.q), dev_bf16(case.kcache), dev_bf16(case.vcache)
+    lens = dev_i32(case.seqlens)
+    bt = dev_i32(case.block_table) if case.paged else None
+    return fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=case.max_kv_len, scale=case.scale,
+                     tokens_per_split=tps)
+
+
+def oracle_out(case):
+    q, kc, vc = (workloads.bf16_bits_to_f64(x) for x in (case.q, case.kcache, case.vcache))
+    o, _ = oracle.decode(q, kc, vc, case.seqlens, case.scale, block_table=case.block_table,
+                         max_kv_len=case.max_kv_len)
+    return o
+
+
+def test_contiguous_decode_32k_full_size():
+    case = workloads.decode_contig_32k()
+    o = run(case)
+    assert_bf16_close(host_f64(o), oracle_out(case), case.name)
+
+
+def test_paged_decode_mixed_lengths_full_size():
+    case = workloads.decode_paged_mixed()
+    o = run(case)
+    assert_bf16_close(host_f64(o), oracle_out(case), case.name)
+
+
+def test_long_context_paged_decode_256k_full_size():
+    case = workloads.decode_long_256k()
+    assert case.max_kv_len // 512 >= 256  # at least 256 splits merged
+    o = run(case)
+    assert_bf16_close(host_f64(o), oracle_out(case), case.name)
+
+
+def test_paged_equals_contiguous_bitwise_32k():
+    """The contiguous 32k cache scattered into a shuffled page pool: same bits out."""
+    case = workloads.decode_contig_32k()
+    paged = workloads.paged_from_contiguous(case)
+    o1 = run(case)
+    o2 = run(paged)
+    assert np.array_equal(host_bits(o1), host_bits(o2))
+
+
+def test_contiguous_equals_paged_bitwise_mixed():
+    """The mixed-length page pool gathered into a padded contiguous cache (on the
+    device, by plain indexing): same bits out, for two split sizes."""
+    torch = torch_gpu()
+    case = workloads.decode_paged_mixed()
+    B, L = case.B, case.max_kv_len
+    pool_k, pool_v = dev_bf16(case.kcache), dev_bf16(case.vcache)
+    bt = dev_i32(case.block_table).long()
+    kc = pool_k[bt.reshape(-1)].reshape(B, L, case.Hkv, case.d).contiguous()
+    vc = pool_v[bt.reshape(-1)].reshape(B, L, case.Hkv, case.d).contiguous()
+    q, lens = dev_bf16(case.q), dev_i32(case.seqlens)
+    for tps in (0, 256):
+        o_paged = run(case, tps)
+        o_contig = fa.decode(q, kc, vc, lens, max_kv_len=L, scale=case.scale, tokens_per_split=tps)
+        assert np.array_equal(host_bits(o_paged), host_bits(o_contig))
+
+
+def test_poisoned_slots_do_not_leak():
+    """NaN in tail slots past each length and in unused pages: output finite and
+    bitwise equal to the unpoisoned run; canaries around o unchanged."""
+    torch = torch_gpu()
+    lens = np.array([1, 15, 16, 17, 31, 33, 100, 513], np.int32)
+    clean = workloads.decode_paged(8, 8, 2, 128, lens, 640, seed=21)
+    dirty = workloads.decode_paged(8, 8, 2, 128, lens, 640, seed=21, poison=True)
+    o_clean = run(clean)
+    q, kc, vc = dev_bf16(dirty.q), dev_bf16(dirty.kcache), dev_bf16(dirty.vcache)
+    n = q.numel()
+    buf = torch.full((n + 512,), -77.0, dtype=torch.bfloat16, device="cuda")
+    o = buf[256:256 + n].view(q.shape)
+    fa.decode(q, kc, vc, dev_i32(dirty.seqlens), block_table=dev_i32(dirty.block_table), max_kv_len=640,
+              scale=dirty.scale, o=o)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:256] == -77.0) and torch.all(buf[256 + n:] == -77.0)
+    assert np.array_equal(host_bits(o), host_bits(o_clean))
+    assert_bf16_close(host_f64(o), oracle_out(clean), "poisoned")
+
+
+def test_contiguous_poisoned_tail():
+    lens = np.array([0, 1, 47, 64], np.int32)
+    case = workloads.decode_contiguous(4, 4, 4, 64, 64, seqlens=lens, seed=22, poison=True)
+    o = run(case)
+    got = host_f64(o)
+    assert np.all(got[0] == 0.0)  # length 0: empty sum
+    assert_bf16_close(got, oracle_out(case), case.name)
+
+
+@pytest.mark.parametrize("G,Hkv,d", [(1, 4, 128), (4, 2, 64), (8, 1, 128), (16, 1, 128), (32, 1, 128), (5, 2, 64)])
+@pytest.mark.parametrize("tps", [0, 32, 1024])
+def test_head_groups_and_split_sizes(G, Hkv, d, tps):
+    lens = np.array([1, 16, 200, 1500], np.int32)
+    case = workloads.decode_paged(4, G * Hkv, Hkv, d, lens, 1536, seed=G * 100 + d + tps)
+    o = run(case, tps)
+    assert_bf16_close(host_f64(o), oracle_out(case), f"{case.name} G={G} tps={tps}")
+
+
+def test_seqlens_clamped_to_capacity():
+    lens = np.array([5000, -3], np.int32)  # above capacity and negative
+    case = workloads.decode_contiguous(2, 4, 2, 128, 96, seqlens=lens, seed=23)
+    o = run(case)
+    got = host_f64(o)
+    assert np.all(got[1] == 0.0)
+    assert_bf16_close(got, oracle_out(case), "clamped")
+
+
+def test_decode_equals_last_row_of_causal_prefill():
+    """One decode step over L cached tokens equals row L-1 of a causal prefill
+    over the same keys (both against the oracle and with each other)."""
+    torch = torch_gpu()
+    L, Hq, Hkv, d = 700, 8, 2, 128
+    pc = workloads.prefill_case(1, Hq, Hkv, L, L, d, True, "bf16", seed=24)
+    o_pre = fa.prefill(dev_bf16(pc.q), dev_bf16(pc.k), dev_bf16(pc.v), causal=True, scale=pc.scale)
+    kc = np.ascontiguousarray(pc.k.transpose(0, 2, 1, 3))
+    vc = np.ascontiguousarray(pc.v.transpose(0, 2, 1, 3))
+    o_dec = fa.decode(dev_bf16(np.ascontiguousarray(pc.q[:, :, -1])), dev_bf16(kc), dev_bf16(vc),
+                      dev_i32(np.array([L], np.int32)), scale=pc.scale)
+    ref, _ = oracle.attention(*pc.as_f64(), pc.scale, True)
+    assert_bf16_close(host_f64(o_dec), ref[:, :, -1], "decode")
+    assert np.max(np.abs(host_f64(o_dec) - host_f64(o_pre)[:, :, -1])) <= 2e-2
+
+
+def test_decode_deterministic():
+    case = workloads.decode_paged(2, 16, 2, 128, np.array([3000, 777], np.int32), 4096, seed=25)
+    assert np.array_equal(host_bits(run(case)), host_bits(run(case)))
+
+
+def test_merge_lse_against_oracle():
+    torch = torch_gpu()
+    rng = np.random.default_rng(26)
+    R, S, d = 37, 19, 128
+    op = rng.standard_normal((R, S, d)).astype(np.float32)
+    ls = (rng.standard_normal((R, S)) * 4).astype(np.float32)
+    ls[3, :5] = -np.inf
+    op[3, :5] = np.nan  # empty splits are never read
+    ls[7, :] = -np.inf  # all-empty row
+    o, lse_out = fa.merge_lse(dev_f32(op), dev_f32(ls), out_dtype=torch.float32)
+    ref_o, ref_l = oracle.merge(op.astype(np.float64), ls.astype(np.float64))
+    got = host_f64(o)
+    assert np.all(got[7] == 0.0) and np.isneginf(host_f64(lse_out)[7])
+    ok = np.arange(R) != 7
+    assert np.max(np.abs(got[ok] - ref_o[ok])) < 2e-5
+    assert np.max(np.abs(host_f64(lse_out)[ok] - ref_l[ok])) < 2e-5
+    ob, _ = fa.merge_lse(dev_f32(op), dev_f32(ls))
+    assert_bf16_close(host_f64(ob)[ok], ref_o[ok], "merge bf16")
+
+
+def test_merge_rejects_page_sum():
+    """Constant value rows over many splits: the merge returns that row (the
+    paged sketch's per-page sum would return it times the split count)."""
+    torch = torch_gpu()
+    u = np.random.default_rng(27).standard_normal(64).astype(np.float32)
+    S = 9
+    op = np.broadcast_to(u, (2, S, 64)).copy()
+    ls = np.random.default_rng(28).standard_normal((2, S)).astype(np.float32)
+    o, _ = fa.merge_lse(dev_f32(op), dev_f32(ls), out_dtype=torch.float32)
+    assert np.max(np.abs(host_f64(o) - u)) < 1e-6
