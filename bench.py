@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused-attention hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Headline (``value``): causal GQA prefill, B=1, Hq=32, Hkv=8, Sq=Skv=2048,
+d=128, bf16 -- algorithmic TFLOP/s over exactly K back-to-back calls of
+fa_prefill (inputs resident in HBM, bracketed by device synchronisation).
+Also reported on the same JSON line:
+  - roofline of the prefill kernel: algorithmic FLOP per launch / mean launch
+    duration (HIP events on the launch stream) against the bf16 dense MFMA peak;
+    HBM traffic from the committed rocprofv3 counter summary when it was taken
+    on the current kernel source, else null;
+  - decode: contiguous 32k (B=4), paged mixed lengths (B=8) and long-context
+    256k (B=1): us/call (both kernels) and algorithmic HBM GB/s against 8 TB/s,
+    each call timed alone after a 1 GiB write that evicts the 256 MB
+    last-level cache;
+  - us/call at B=1 for the fp32 single-head prefill and the bf16 prefill;
+  - cpu_baseline: the fp64 oracle on the full prefill workload, host cores.
+Only one GPU is used; --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "prefill attn TFLOP/s + decode HBM GB/s (% of peak); µs/call at B=1"
+PREFILL_KERNEL_SRC = os.path.join(ROOT, "attention_fa_prefill_amd", "csrc", "prefill_bf16.hip")
+DECODE_KERNEL_SRC = os.path.join(ROOT, "attention_fa_prefill_amd", "csrc", "decode.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def prefill_flops(B, Hq, Sq, Skv, d, causal):
+    """Algorithmic FLOPs: 2*d for q.k plus 2*d for p*v per visible (query, key)."""
+    if causal:
+        off = Skv - Sq
+        vis = sum(min(Skv, i + off + 1) for i in range(Sq))
+    else:
+        vis = Sq * Skv
+    return 4 * d * Hq * B * vis
+
+
+def prefill_bytes(B, Hq, Hkv, Sq, Skv, d, elt=2):
+    return elt * (2 * B * Hq * Sq * d + 2 * B * Hkv * Skv * d)
+
+
+def decode_bytes(case):
+    """Algorithmic bytes: every cached K and V row once, q and o, seqlens, and the
+    block-table entries of the pages used."""
+    import numpy as np
+
+    lens = np.clip(case.seqlens, 0, case.max_kv_len).astype(np.int64)
+    b = 2 * (2 * case.Hkv * case.d * int(lens.sum()) + 2 * case.B * case.Hq * case.d) + 4 * case.B
+    if case.paged:
+        b += 4 * int(((lens + 15) // 16).sum())
+    return b
+
+
+def sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_key, src_path):
+    """HBM bytes per launch from the committed counter summary, if it was taken on
+    the current kernel source; else None."""
+    try:
+        with open(COUNTERS) as f:
+            data = json.load(f)
+        ent = data[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if ent.get("source_sha") != sha(src_path):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="skip the decode and latency legs")
+    ap.add_argument("--decode-reps", type=int, default=50)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path does not "
+              f"shard across GPUs).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import attention_fa_prefill_amd as fa
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(x):
+        return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
+
+    # ------------------------------------------------------------------ headline: GQA causal prefill
+    case = workloads.prefill_gqa_2k()
+    q, k, v = bf16(case.q), bf16(case.k), bf16(case.v)
+    o = torch.empty_like(q)
+    L = fa.lib()
+    B, Hq, Hkv, Sq, Skv, d = case.B, case.Hq, case.Hkv, case.Sq, case.Skv, case.d
+    hstream = ctypes_stream = None
+    import ctypes
+
+    ctypes_stream = ctypes.c_void_p(stream.cuda_stream)
+    argv = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(o.data_ptr()), B, Hq, Hkv, Sq, Skv, d, case.scale, 1, ctypes_stream)
+
+    def step():
+        st = L.fa_prefill(*argv)
+        if st != 0:
+            raise RuntimeError(fa.status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / K
+    flops = prefill_flops(B, Hq, Sq, Skv, d, True)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    mean_launch_ms = statistics.fmean(launch_ms)
+    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+    traffic = traffic_for("prefill_bf16_kernel<128>@prefill_gqa_b1h32x8s2048d128", PREFILL_KERNEL_SRC)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "prefill_bf16_kernel<128>", "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                "algorithmic_flop_per_launch": flops,
+                "algorithmic_bytes_per_launch": prefill_bytes(B, Hq, Hkv, Sq, Skv, d)}
+
+    result = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+              "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+              "config": {"workload": case.name, "B": B, "Hq": Hq, "Hkv": Hkv, "Sq": Sq, "Skv": Skv, "d": d,
+                         "causal": True, "scale": case.scale, "seed": 1002},
+              "roofline": roofline,
+              "prefill_us_per_call_p50": round(statistics.median(launch_ms) * 1e3, 2)}
+
+    # ------------------------------------------------------------------ decode and latency legs
+    if not args.prefill_only:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+        def timed_calls(fn, reps, evict):
+            times = []
+            for _ in range(3):
+                fn()
+            for _ in range(reps):
+                if evict:
+                    flush.fill_(1)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                b.synchronize()
+                times.append(a.elapsed_time(b) * 1e3)
+            return times
+
+        dec = {}
+        for dc in (workloads.decode_contig_32k(), workloads.decode_paged_mixed(), workloads.decode_long_256k()):
+            dq, dk, dv = bf16(dc.q), bf16(dc.kcache), bf16(dc.vcache)
+            lens = i32(dc.seqlens)
+            bt = i32(dc.block_table) if dc.paged else None
+            od = torch.empty_like(dq)
+            need = fa.decode_workspace_bytes(dc.B, dc.Hq, dc.d, dc.max_kv_len, 0)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            dargs = (ctypes.c_void_p(dq.data_ptr()), ctypes.c_void_p(dk.data_ptr()), ctypes.c_void_p(dv.data_ptr()),
+                     ctypes.c_void_p(bt.data_ptr()) if bt is not None else None, ctypes.c_void_p(lens.data_ptr()),
+                     ctypes.c_void_p(od.data_ptr()), dc.B, dc.Hq, dc.Hkv, dc.d, dc.max_kv_len,
+                     16 if dc.paged else 0, 0, dc.scale, ctypes.c_void_p(ws.data_ptr()), need, ctypes_stream)
+
+            def dcall(dargs=dargs):
+                st = L.fa_decode(*dargs)
+                if st != 0:
+                    raise RuntimeError(fa.status_string(st))
+
+            t = timed_calls(dcall, args.decode_reps, evict=True)
+            t_warm = timed_calls(dcall, 20, evict=False)
+            nbytes = decode_bytes(dc)
+            p50 = statistics.median(t)
+            dec[dc.name] = {"us_per_call_p50": round(p50, 2), "us_p10": round(float(np.percentile(t, 10)), 2),
+                            "us_p90": round(float(np.percentile(t, 90)), 2),
+                            "GB_per_s": round(nbytes / (p50 * 1e-6) / 1e9, 1),
+                            "frac_of_hbm_peak": round(nbytes / (p50 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                            "algorithmic_bytes": nbytes, "cache_evicted": True,
+                            "us_per_call_p50_warm": round(statistics.median(t_warm), 2),
+                            "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "d": dc.d, "tokens": dc.total_tokens(),
+                            "paged": dc.paged, "tokens_per_split": 512}
+            del dq, dk, dv, ws, od, lens, bt
+            torch.cuda.empty_cache()
+        result["decode"] = dec
+        traffic_dec = traffic_for("decode_split_kernel<128>@decode_long_b1h16x2kv256kd128", DECODE_KERNEL_SRC)
+        long = dec["decode_long_b1h16x2kv256kd128"]
+        result["roofline_decode"] = {"bound": "hbm", "achieved": long["GB_per_s"], "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": long["frac_of_hbm_peak"], "traffic": traffic_dec,
+                                     "workload": "decode_long_b1h16x2kv256kd128",
+                                     "note": "split + merge kernels per call, cache evicted before each call"}
+
+        # fp32 single-head causal prefill at B=1 (launch-latency bound)
+        c1 = workloads.prefill_f32_small()
+        q1 = torch.from_numpy(c1.q).to(dev)
+        k1 = torch.from_numpy(c1.k).to(dev)
+        v1 = torch.from_numpy(c1.v).to(dev)
+        o1 = torch.empty_like(q1)
+        a1 = (ctypes.c_void_p(q1.data_ptr()), ctypes.c_void_p(k1.data_ptr()), ctypes.c_void_p(v1.data_ptr()),
+              ctypes.c_void_p(o1.data_ptr()), 1, 1, 1, 128, 128, 64, c1.scale, 1, ctypes_stream)
+
+        def c1call():
+            st = L.fa_prefill_f32(*a1)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+
+        t1 = timed_calls(c1call, 200, evict=False)
+        # empty-work floor: the same stream, a 1-element fill (one trivial kernel)
+        tiny = torch.empty(1, device=dev)
+        tf = timed_calls(lambda: tiny.fill_(0.0), 200, evict=False)
+        result["latency_b1"] = {
+            c1.name: {"us_per_call_p50": round(statistics.median(t1), 2),
+                      "us_p10": round(float(np.percentile(t1, 10)), 2)},
+            "single_trivial_kernel_floor_us_p50": round(statistics.median(tf), 2),
+            case.name: {"us_per_call_p50": result["prefill_us_per_call_p50"]},
+            "decode_long_b1h16x2kv256kd128": {"us_per_call_p50": long["us_per_call_p50"]},
+        }
+
+    # ------------------------------------------------------------------ CPU baseline: the oracle
+    if not args.no_cpu_baseline:
+        import oracle
+
+        qf, kf, vf = case.as_f64()
+        t0 = time.perf_counter()
+        oracle.attention(qf, kf, vf, case.scale, True)
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s",
+                                  "cores": oracle.num_threads(), "kind": "oracle",
+                                  "sample": f"the whole {case.name} workload once (fp64, {dt:.2f} s wall)"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
