@@ -38,7 +38,10 @@ fa::PrefillParams make_prefill(const void* q, const void* k, const void* v, void
   fa::PrefillParams p;
   p.q = q; p.k = k; p.v = v; p.o = o;
   p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Sq = Sq; p.Skv = Skv;
-  p.c = fabsf(scale) * fa::kLog2e;
+  // c = |scale| * log2(e), kept >= 1e-30: with scale = 0 every score scales to
+  // ~0 (uniform weights, as the definition gives) while a masked score of -inf
+  // still scales to -inf, so exp2 returns exactly 0 for it.
+  p.c = fmaxf(fabsf(scale) * fa::kLog2e, 1e-30f);
   p.neg = scale < 0.f ? 1 : 0;
   p.causal = causal;
   p.nT = (Sq + 127) / 128;

@@ -70,9 +70,12 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
 // Issue one 64-key K or V block of one group: HBM -> LDS, 16 bytes per lane.
@@ -106,7 +109,9 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[2 * C::ELEMS];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform across the wave: keep it (and everything derived
+  // from it) in scalar registers so that per-wave decisions are scalar branches.
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wave >> 2;  // 0 = group A, 1 = group B
   const int wg = wave & 3;    // wave within group
   const int hl = lane >> 5;   // half-wave
@@ -118,7 +123,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   const bool causal = p.causal != 0;
   const float c = p.c;
 
-  auto nblocks = [&](int t) {
+  auto nblocks = [&](int t) __attribute__((always_inline)) {
     const int end = causal ? min(Skv, (t + 1) * kBM + off) : Skv;
     return (end + kBN - 1) / kBN;
   };
@@ -130,19 +135,50 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   const bool split = jB < n1;                  // group A holds a partial of t1
   const int cnt = grp ? cntB : cntA;
   const int maxcnt = max(cntA, cntB);
+  auto kv_of = [&](int i) __attribute__((always_inline)) { return grp ? i : (i < nA0 ? i : jB + (i - nA0)); };
 
   const __bf16* kbh = (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
   const __bf16* vbh = (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
 
-  auto kv_of = [&](int i) { return grp ? i : (i < nA0 ? i : jB + (i - nA0)); };
-  auto tile_of = [&](int i) { return grp ? t1 : (i < nA0 ? t0 : t1); };
+  // Per-lane byte offsets (inside a 64-key block) of this lane's direct-to-LDS
+  // loads: LDS chunk P of the block holds logical chunk (P % CH) ^ swz(row) of
+  // row P / CH. Loop-invariant, so a full block costs one scalar base per load.
+  uint32_t koff[C::NI], voff[C::NI];
+#pragma unroll
+  for (int ii = 0; ii < C::NI; ++ii) {
+    const int P = 64 * (wg * C::NI + ii) + lane;
+    const int row = P / C::CH, pc = P % C::CH;
+    koff[ii] = (uint32_t)(row * D + ((pc ^ swz_k<D>(row)) << 3)) * 2u;
+    voff[ii] = (uint32_t)(row * D + ((pc ^ swz_v<D>(row)) << 3)) * 2u;
+  }
+  auto dma = [&](__bf16* sK, __bf16* sV, int j) __attribute__((always_inline)) {
+    const int kv0 = j * kBN;
+    __bf16* kd = sK + grp * C::ELEMS;
+    __bf16* vd = sV + grp * C::ELEMS;
+    if (kv0 + kBN <= Skv) {
+      const char* kb = (const char*)(kbh + (size_t)kv0 * D);
+      const char* vb = (const char*)(vbh + (size_t)kv0 * D);
+#pragma unroll
+      for (int ii = 0; ii < C::NI; ++ii) {
+        __bf16* dst = 64 * (wg * C::NI + ii) * 8 + kd;
+        __builtin_amdgcn_global_load_lds((const void*)(kb + koff[ii]), (lds_void_t*)dst, 16, 0, 0);
+      }
+#pragma unroll
+      for (int ii = 0; ii < C::NI; ++ii) {
+        __bf16* dst = 64 * (wg * C::NI + ii) * 8 + vd;
+        __builtin_amdgcn_global_load_lds((const void*)(vb + voff[ii]), (lds_void_t*)dst, 16, 0, 0);
+      }
+    } else {
+      dma_block<D, false>(kbh, kd, kv0, Skv, wg, lane);
+      dma_block<D, true>(vbh, vd, kv0, Skv, wg, lane);
+    }
+  };
 
   f32x16 O[C::DB];
   bf16x8 qreg[C::KS];
   float m_run = -INFINITY, l_run = 0.f;
-  int cur_tile = -1;
 
-  auto reset_state = [&]() {
+  auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -152,7 +188,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   };
 
   // Q^T operand: lane holds Q[row ln][16 ks + 8 hl .. +8] for every k-step.
-  auto load_q = [&](int t) {
+  auto load_q = [&](int t) __attribute__((always_inline)) {
     const int row = t * kBM + wg * 32 + ln;
     const uint32_t flip = p.neg ? 0x80008000u : 0u;
 #pragma unroll
@@ -167,7 +203,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     }
   };
 
-  auto store_tile = [&](int t) {
+  auto store_tile = [&](int t) __attribute__((always_inline)) {
     const float lt = pair_sum(l_run);
     const float inv = 1.0f / lt;
     const int row = t * kBM + wg * 32 + ln;
@@ -185,48 +221,26 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     }
   };
 
-  // One 64-key block of the current tile for this wave, from LDS stage (sK, sV).
-  auto compute = [&](const __bf16* sK, const __bf16* sV, int t, int j) {
-    const int q0 = t * kBM + wg * 32;  // first query row of this wave
-    const int kv0 = j * kBN;
-    const char* kbase = (const char*)(sK + grp * C::ELEMS);
-    const char* vbase = (const char*)(sV + grp * C::ELEMS);
-    bool act[2], msk[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kb = kv0 + 32 * sub;
-      act[sub] = kb < Skv && (!causal || kb <= q0 + 31 + off);
-      msk[sub] = (kb + 31 >= Skv) || (causal && kb + 31 > q0 + off);
-    }
-    f32x16 S[2];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      S[sub] = f32x16{};
-      if (!act[sub]) continue;
-      const int row = 32 * sub + ln;
-      const char* krow = kbase + row * (D * 2);
-#pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) {
-        const int ch = (2 * ks + hl) ^ swz_k<D>(row);
-        const bf16x8 a = *(const bf16x8*)(krow + ch * 16);
-        S[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], S[sub], 0, 0, 0);
-      }
-      if (msk[sub]) {
-        const int qrow = q0 + ln;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + 32 * sub + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool vis = key < Skv && (!causal || key <= qrow + off);
-          if (!vis) S[sub][r] = -INFINITY;
-        }
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-      if (act[sub])
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sub][r]);
+  const int kr0 = ln * (D * 2), kr1 = (32 + ln) * (D * 2);
+  const int sw0 = swz_k<D>(ln), sw1 = swz_k<D>(32 + ln);
+  auto kread = [&](const char* kbase, int kr, int sw, int ks) __attribute__((always_inline)) {
+    return *(const bf16x8*)(kbase + kr + (((2 * ks + hl) ^ sw) << 4));
+  };
+  // V^T operand rows/columns (transpose reads): see the header comment.
+  const int gg = lane >> 4, jj = lane & 15, dh = gg & 1;
+  auto vread = [&](const char* vbase, int sub, int s, int db) __attribute__((always_inline)) {
+    const int row1 = 32 * sub + 16 * s + 4 * hl + (jj >> 2);
+    const int row2 = row1 + 8;
+    const int colb = (32 * db + 16 * dh + 4 * (jj & 3)) * 2;
+    const char* a1 = vbase + row1 * (D * 2) + (((colb >> 4) ^ swz_v<D>(row1)) << 4) + (colb & 15);
+    const char* a2 = vbase + row2 * (D * 2) + (((colb >> 4) ^ swz_v<D>(row2)) << 4) + (colb & 15);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  // Online-softmax update from the tile max; returns the rescale factor.
+  auto update_max = [&](float mx) __attribute__((always_inline)) {
     mx = pair_max(mx);
     const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
     float alpha = 1.f;
@@ -234,29 +248,9 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
       alpha = fast_exp2(m_run - cand);
       m_run = cand;
     }
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-    bf16x8 P[2][2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (!act[sub]) continue;
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        e[r] = fast_exp2(fmaf(S[sub][r], c, -mu));
-        if (msk[sub] && S[sub][r] == -INFINITY) e[r] = 0.f;
-        lsum += e[r];
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        uint4 w;
-        w.x = pack_bf16x2(e[8 * s + 0], e[8 * s + 1]);
-        w.y = pack_bf16x2(e[8 * s + 2], e[8 * s + 3]);
-        w.z = pack_bf16x2(e[8 * s + 4], e[8 * s + 5]);
-        w.w = pack_bf16x2(e[8 * s + 6], e[8 * s + 7]);
-        P[sub][s] = __builtin_bit_cast(bf16x8, w);
-      }
-    }
+    return alpha;
+  };
+  auto rescale = [&](float alpha, float lsum) __attribute__((always_inline)) {
     l_run = alpha * l_run + lsum;
     if (__any(alpha != 1.f)) {
 #pragma unroll
@@ -264,81 +258,133 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
-    // O^T += V^T . P^T
-    const int gg = lane >> 4, jj = lane & 15, dh = gg & 1;
+  };
+  // exp2, row-sum and bf16 packing of one 32-key sub-tile. Masked scores are
+  // -inf and come out as exactly 0 (c > 0 and mu finite).
+  auto probs = [&](const f32x16& Ssub, float mu, bf16x8* P2, float& la, float& lb) __attribute__((always_inline)) {
+    float e[16];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      if (!act[sub]) continue;
+    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(Ssub[r], c, -mu));
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const int row1 = 32 * sub + 16 * s + 4 * hl + (jj >> 2);
-        const int row2 = row1 + 8;
+    for (int r = 0; r < 16; r += 2) { la += e[r]; lb += e[r + 1]; }
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-          const int colb = (32 * db + 16 * dh + 4 * (jj & 3)) * 2;  // byte column
-          const char* a1 = vbase + row1 * (D * 2) + (((colb >> 4) ^ swz_v<D>(row1)) << 4) + (colb & 15);
-          const char* a2 = vbase + row2 * (D * 2) + (((colb >> 4) ^ swz_v<D>(row2)) << 4) + (colb & 15);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[sub][s], O[db], 0, 0, 0);
-        }
+    for (int s = 0; s < 2; ++s) {
+      uint4 w;
+      w.x = pack_bf16x2(e[8 * s + 0], e[8 * s + 1]);
+      w.y = pack_bf16x2(e[8 * s + 2], e[8 * s + 3]);
+      w.z = pack_bf16x2(e[8 * s + 4], e[8 * s + 5]);
+      w.w = pack_bf16x2(e[8 * s + 6], e[8 * s + 7]);
+      P2[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+  auto pv = [&](const char* vbase, int sub, const bf16x8* P2) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8 a = vread(vbase, sub, s, 0);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        bf16x8 an = a;
+        if (db + 1 < C::DB) an = vread(vbase, sub, s, db + 1);
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P2[s], O[db], 0, 0, 0);
+        a = an;
       }
     }
   };
 
-  auto begin_tile_if_needed = [&](int i) {
-    const int t = tile_of(i);
-    if (t != cur_tile) {
-      if (cur_tile >= 0) store_tile(cur_tile);
-      reset_state();
-      load_q(t);
-      cur_tile = t;
+  // One 64-key block for this wave's 32 rows. Blocks that some row sees only
+  // partly (causal diagonal, end of the keys) get their invisible scores set to
+  // -inf behind a wave-uniform branch; a block no row of the wave sees is skipped.
+  auto block = [&](const __bf16* sK, const __bf16* sV, int q0, int kv0) __attribute__((always_inline)) {
+    if (kv0 >= Skv || (causal && kv0 > q0 + 31 + off)) return;
+    const char* kbase = (const char*)(sK + grp * C::ELEMS);
+    const char* vbase = (const char*)(sV + grp * C::ELEMS);
+    f32x16 S0 = f32x16{}, S1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const bf16x8 a0 = kread(kbase, kr0, sw0, ks);
+      const bf16x8 a1 = kread(kbase, kr1, sw1, ks);
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], S1, 0, 0, 0);
+    }
+    const bool full = kv0 + kBN <= Skv && (!causal || kv0 + kBN - 1 <= q0 + off);
+    if (!full) {
+      // key of register r of sub-tile u is kb + 8*(r/4) + (r%4), kb = kv0 + 32u + 4hl;
+      // visible iff < Skv and (non-causal or) <= query row + off
+      const int kb = kv0 + 4 * hl;
+      int lim = Skv - 1 - kb;
+      if (causal) lim = min(lim, q0 + ln + off - kb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ko = 8 * (r >> 2) + (r & 3);
+        if (ko > lim) S0[r] = -INFINITY;
+        if (ko + 32 > lim) S1[r] = -INFINITY;
+      }
+    }
+    float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+    const float alpha = update_max(mx);
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    bf16x8 P0[2], P1[2];
+    float la = 0.f, lb = 0.f;
+    probs(S0, mu, P0, la, lb);
+    probs(S1, mu, P1, la, lb);
+    rescale(alpha, la + lb);
+    pv(vbase, 0, P0);
+    pv(vbase, 1, P1);
+  };
+
+  // One iteration: barrier, prefetch the next block into the other stage,
+  // consume this block. (sKc, sVc) is this iteration's stage.
+  auto body = [&](int i, int t, __bf16* sKc, __bf16* sVc, __bf16* sKn, __bf16* sVn) __attribute__((always_inline)) {
+    __syncthreads();
+    if (i + 1 < cnt) dma(sKn, sVn, kv_of(i + 1));
+    block(sKc, sVc, t * kBM + wg * 32, kv_of(i) * kBN);
+  };
+  // Iterations [i0, i1) of this group, all on tile t; the stage is the
+  // iteration's parity (the loop walks aligned pairs and skips iterations
+  // outside the range, so each stage's code appears once).
+  auto run = [&](int i0, int i1, int t) __attribute__((always_inline)) {
+    for (int i = i0 & ~1; i < i1; i += 2) {
+      if (i >= i0) body(i, t, sK0, sV0, sK1, sV1);
+      if (i + 1 < i1) body(i + 1, t, sK1, sV1, sK0, sV0);
     }
   };
 
-  // ---- main loop: stage 0 / stage 1 alternate; one barrier per block.
-  if (cnt > 0) {
-    dma_block<D, false>(kbh, sK0 + grp * C::ELEMS, kv_of(0) * kBN, Skv, wg, lane);
-    dma_block<D, true>(vbh, sV0 + grp * C::ELEMS, kv_of(0) * kBN, Skv, wg, lane);
+  // ---- main loops: both groups execute exactly maxcnt barriers.
+  // Group A: phase 0 = all of t0, phase 1 = the tail of t1's KV range.
+  // Group B: phase 0 = the head of t1's KV range.
+  if (cnt > 0) dma(sK0, sV0, kv_of(0));
+  for (int phase = 0; phase < 2; ++phase) {
+    int i0, i1, t;
+    if (grp == 0) {
+      i0 = phase ? nA0 : 0;
+      i1 = phase ? cntA : nA0;
+      t = phase ? t1 : t0;
+    } else {
+      i0 = 0;
+      i1 = phase ? 0 : cntB;
+      t = t1;
+    }
+    if (i0 >= i1) continue;
+    reset_state();
+    load_q(t);
+    run(i0, i1, t);
+    if (grp == 0 && phase == 0) store_tile(t0);
   }
-  for (int i = 0; i < maxcnt; i += 2) {
-    __syncthreads();
-    if (i + 1 < cnt) {
-      dma_block<D, false>(kbh, sK1 + grp * C::ELEMS, kv_of(i + 1) * kBN, Skv, wg, lane);
-      dma_block<D, true>(vbh, sV1 + grp * C::ELEMS, kv_of(i + 1) * kBN, Skv, wg, lane);
-    }
-    if (i < cnt) {
-      begin_tile_if_needed(i);
-      compute(sK0, sV0, tile_of(i), kv_of(i));
-    }
-    if (i + 1 >= maxcnt) break;
-    __syncthreads();
-    if (i + 2 < cnt) {
-      dma_block<D, false>(kbh, sK0 + grp * C::ELEMS, kv_of(i + 2) * kBN, Skv, wg, lane);
-      dma_block<D, true>(vbh, sV0 + grp * C::ELEMS, kv_of(i + 2) * kBN, Skv, wg, lane);
-    }
-    if (i + 1 < cnt) {
-      begin_tile_if_needed(i + 1);
-      compute(sK1, sV1, tile_of(i + 1), kv_of(i + 1));
-    }
-  }
+  for (int i = cnt; i < maxcnt; ++i) __syncthreads();
 
   // ---- epilogue: group A hands its partial of t1 to group B through LDS.
   __syncthreads();
   float* xo = (float*)((wg < 2 ? (char*)sK0 : (char*)sV0)) + (wg & 1) * C::XO;
   float* xml = (float*)sK1 + wg * 128;
-  if (grp == 0) {
-    if (split) {
+  if (grp == 0 && split) {
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = O[db][r];
-      xml[lane * 2 + 0] = m_run;
-      xml[lane * 2 + 1] = l_run;
-    } else if (cur_tile >= 0) {
-      store_tile(cur_tile);
-    }
+      for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = O[db][r];
+    xml[lane * 2 + 0] = m_run;
+    xml[lane * 2 + 1] = l_run;
   }
   __syncthreads();
   if (grp == 1) {

@@ -94,6 +94,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode and latency legs")
     ap.add_argument("--decode-reps", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run 5 plain 256 MiB device-to-device copies (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (this path does not "
@@ -110,6 +112,16 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.copy_calibration:
+        # a plain copy of known size: 256 MiB read + 256 MiB written per dispatch
+        src = torch.ones(1 << 28, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": 1 << 28, "dispatches": 5}), flush=True)
+        return
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
