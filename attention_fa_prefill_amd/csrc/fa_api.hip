@@ -30,6 +30,9 @@ fa_status check_prefill(const void* q, const void* k, const void* v, void* o, in
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
+  // the bf16 kernel runs one work-group per (pair of 128-row query tiles, head, batch)
+  const long pairs = ((long)Sq + 255) / 256;
+  if (pairs * Hq * B > (long)INT32_MAX) return FA_ERR_SHAPE;
   return FA_OK;
 }
 

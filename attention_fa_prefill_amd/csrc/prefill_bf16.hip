@@ -15,9 +15,11 @@
 //     the same work. Group B runs the first half of t1's KV range; group A runs
 //     all of t0 and then the rest of t1's range; the two partial states of t1
 //     (m, l, O) are merged through LDS. Every work-group gets the same work.
-//   - K/V blocks of 64 keys go HBM -> LDS with 16-byte direct-to-LDS loads
-//     (global_load_lds_dwordx4), double-buffered per group; the next block is in
-//     flight while the current one is consumed.
+//   - work-groups are ordered so that all query heads sharing a kv head run on
+//     one XCD (work-group L runs on XCD L % 8): each K/V block is fetched from
+//     HBM into one L2 and reused there.
+//   - K/V blocks of 64 keys go HBM/L2 -> LDS with 16-byte direct-to-LDS buffer
+//     loads, double-buffered per group, issued two slots ahead of their use.
 //
 // Per wave and per 64-key block (two 32-key sub-tiles):
 //   S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T held
@@ -29,6 +31,14 @@
 //   O^T += V^T . P^T on the same MFMA: A = V^T read with ds_read_b64_tr_b16
 //   from the row-major V tile in LDS, B = P^T straight from the score registers
 //   (the contraction order over keys is permuted to match their lane layout).
+//
+// Ping-pong schedule. A wave alternates two kinds of slot: an MFMA slot
+// M(k) = { O += V(k-1)^T P(k-1)^T ; S(k) = K(k) Q^T } and a vector slot
+// V(k) = { softmax of S(k) -> P(k) }. Group B runs half an iteration behind
+// group A, and the groups swap slot kinds at every barrier, so on each SIMD one
+// wave issues MFMA while the other issues the softmax. The barriers only order
+// LDS (no wait for outstanding HBM loads): a group waits for its own
+// direct-to-LDS loads right before the barrier that opens its next MFMA slot.
 #include "fa_internal.h"
 
 namespace fa {
@@ -37,6 +47,8 @@ namespace {
 constexpr int kBM = 128;     // query rows per wave group
 constexpr int kBN = 64;      // keys per KV block
 constexpr float kTau = 8.0f; // lazy rescale threshold (log2 units)
+constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 template <int D>
 struct Cfg {
@@ -46,11 +58,12 @@ struct Cfg {
   static constexpr int KS = D / 16;              // k-steps of S^T = K . Q^T
   static constexpr int DB = D / 32;              // 32-row d blocks of O^T
   static constexpr int XO = 64 * DB * 16;        // floats of one wave's O^T in the exchange
+  static constexpr int QI = 32 * CH / 64;        // direct-to-LDS loads per wave for its Q rows
 };
 
 // LDS swizzles (16-byte chunk index XOR a function of the row).
-// K rows are read 16 bytes per lane for 16 consecutive rows at one chunk:
-// XOR with row mod CH spreads them over all banks.
+// K (and staged Q) rows are read 16 bytes per lane for 16 consecutive rows at
+// one chunk: XOR with row mod CH spreads them over all banks.
 template <int D>
 __device__ __forceinline__ int swz_k(int row) { return row & (Cfg<D>::CH - 1); }
 // V is read by transpose reads: each 16-lane group touches 4 consecutive rows x
@@ -78,35 +91,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
-// Issue one 64-key K or V block of one group: HBM -> LDS, 16 bytes per lane.
-// LDS chunk P of the block holds logical chunk (P % CH) ^ swz(row) of row
-// P / CH; rows past Skv are clamped to Skv-1 (finite data, masked out later).
-template <int D, bool IS_V>
-__device__ __forceinline__ void dma_block(const __bf16* __restrict__ src_bh, __bf16* lds_block, int kv0, int Skv,
-                                          int wg, int lane) {
-  using C = Cfg<D>;
-#pragma unroll
-  for (int ii = 0; ii < C::NI; ++ii) {
-    const int P = 64 * (wg * C::NI + ii) + lane;
-    const int row = P / C::CH, pc = P % C::CH;
-    const int lc = pc ^ (IS_V ? swz_v<D>(row) : swz_k<D>(row));
-    const int grow = min(kv0 + row, Skv - 1);
-    const __bf16* src = src_bh + (size_t)grow * D + lc * 8;
-    __bf16* dst = lds_block + 64 * (wg * C::NI + ii) * 8;
-    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void_t*)dst, 16, 0, 0);
-  }
+// Barrier that orders LDS only: the wave's LDS reads are complete before it
+// arrives; outstanding HBM loads are not waited for (the caller waits for its
+// own direct-to-LDS loads where their data is needed). The memory clobber
+// keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+__device__ __forceinline__ void wait_dma() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 template <int D>
 __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   using C = Cfg<D>;
-  // Two stages x {K, V}, each holding both groups' blocks. Separate arrays let
-  // the compiler see that the block being loaded never aliases the block being
-  // read, so no wait is inserted between them.
+  // Two stages x {K, V}, each holding both groups' blocks, plus a staging area
+  // for the second query tile of group A. Separate arrays let the compiler see
+  // that a block being loaded never aliases the block being read.
   __shared__ __attribute__((aligned(1024))) __bf16 sK0[2 * C::ELEMS];
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[2 * C::ELEMS];
   __shared__ __attribute__((aligned(1024))) __bf16 sK1[2 * C::ELEMS];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[2 * C::ELEMS];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ[kBM * D];
 
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave: keep it (and everything derived
@@ -116,7 +123,19 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   const int wg = wave & 3;    // wave within group
   const int hl = lane >> 5;   // half-wave
   const int ln = lane & 31;
-  const int pidx = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // XCD-aware work order: work item I (pair fastest, then query head, then
+  // batch) goes to the work-group that puts contiguous item ranges on one XCD.
+  int pidx, h, b;
+  {
+    const int W = p.nP * p.Hq * p.B;
+    const int L = blockIdx.x;
+    const int xcd = L % kXcds, idx = L / kXcds;
+    const int q = W / kXcds, r = W % kXcds;
+    const int I = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+    pidx = I % p.nP;
+    h = (I / p.nP) % p.Hq;
+    b = I / (p.nP * p.Hq);
+  }
   const int g = (int)((long)h * p.Hkv / p.Hq);
   const int Sq = p.Sq, Skv = p.Skv;
   const int off = Skv - Sq;
@@ -134,15 +153,16 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   const int cntA = nA0 + (n1 - jB), cntB = jB;
   const bool split = jB < n1;                  // group A holds a partial of t1
   const int cnt = grp ? cntB : cntA;
-  const int maxcnt = max(cntA, cntB);
   auto kv_of = [&](int i) __attribute__((always_inline)) { return grp ? i : (i < nA0 ? i : jB + (i - nA0)); };
+  auto tile_of = [&](int i) __attribute__((always_inline)) { return grp ? t1 : (i < nA0 ? t0 : t1); };
 
   const __bf16* kbh = (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
   const __bf16* vbh = (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* qbh = (const __bf16*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
 
   // Per-lane byte offsets (inside a 64-key block) of this lane's direct-to-LDS
   // loads: LDS chunk P of the block holds logical chunk (P % CH) ^ swz(row) of
-  // row P / CH. Loop-invariant, so a full block costs one scalar base per load.
+  // row P / CH.
   uint32_t koff[C::NI], voff[C::NI];
 #pragma unroll
   for (int ii = 0; ii < C::NI; ++ii) {
@@ -151,32 +171,24 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     koff[ii] = (uint32_t)(row * D + ((pc ^ swz_k<D>(row)) << 3)) * 2u;
     voff[ii] = (uint32_t)(row * D + ((pc ^ swz_v<D>(row)) << 3)) * 2u;
   }
-  auto dma = [&](__bf16* sK, __bf16* sV, int j) __attribute__((always_inline)) {
+  // One K or V block -> this group's slot of an LDS stage. The buffer resource
+  // covers only the keys that exist, so rows past Skv read as zero.
+  auto dma = [&](const __bf16* src_bh, __bf16* stage, const uint32_t* offs, int j) __attribute__((always_inline)) {
     const int kv0 = j * kBN;
-    __bf16* kd = sK + grp * C::ELEMS;
-    __bf16* vd = sV + grp * C::ELEMS;
-    if (kv0 + kBN <= Skv) {
-      const char* kb = (const char*)(kbh + (size_t)kv0 * D);
-      const char* vb = (const char*)(vbh + (size_t)kv0 * D);
+    const int rows = min(kBN, Skv - kv0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(src_bh + (size_t)kv0 * D), (short)0, rows * D * 2, kRsrcWord3);
+    __bf16* dst0 = stage + grp * C::ELEMS;
 #pragma unroll
-      for (int ii = 0; ii < C::NI; ++ii) {
-        __bf16* dst = 64 * (wg * C::NI + ii) * 8 + kd;
-        __builtin_amdgcn_global_load_lds((const void*)(kb + koff[ii]), (lds_void_t*)dst, 16, 0, 0);
-      }
-#pragma unroll
-      for (int ii = 0; ii < C::NI; ++ii) {
-        __bf16* dst = 64 * (wg * C::NI + ii) * 8 + vd;
-        __builtin_amdgcn_global_load_lds((const void*)(vb + voff[ii]), (lds_void_t*)dst, 16, 0, 0);
-      }
-    } else {
-      dma_block<D, false>(kbh, kd, kv0, Skv, wg, lane);
-      dma_block<D, true>(vbh, vd, kv0, Skv, wg, lane);
-    }
+    for (int ii = 0; ii < C::NI; ++ii)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst0 + 64 * (wg * C::NI + ii) * 8), 16,
+                                               (int)offs[ii], 0, 0, 0);
   };
 
   f32x16 O[C::DB];
   bf16x8 qreg[C::KS];
   float m_run = -INFINITY, l_run = 0.f;
+  int cur_tile = -1;
 
   auto reset_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -187,18 +199,41 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     l_run = 0.f;
   };
 
+  const uint32_t qflip = p.neg ? 0x80008000u : 0u;
   // Q^T operand: lane holds Q[row ln][16 ks + 8 hl .. +8] for every k-step.
-  auto load_q = [&](int t) __attribute__((always_inline)) {
+  auto load_q_global = [&](int t) __attribute__((always_inline)) {
     const int row = t * kBM + wg * 32 + ln;
-    const uint32_t flip = p.neg ? 0x80008000u : 0u;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (row < Sq) {
-        const uint4* src = (const uint4*)((const __bf16*)p.q + (((size_t)b * p.Hq + h) * Sq + row) * D + 16 * ks + 8 * hl);
-        x = *src;
-      }
-      x.x ^= flip; x.y ^= flip; x.z ^= flip; x.w ^= flip;
+      if (row < Sq) x = *(const uint4*)(qbh + (size_t)row * D + 16 * ks + 8 * hl);
+      x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
+      qreg[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  };
+  // Group A stages its second tile's Q rows in LDS at the start (each wave its
+  // own 32 rows), so the tile switch costs LDS reads instead of HBM latency.
+  auto stage_q = [&](int t) __attribute__((always_inline)) {
+    const int row0 = t * kBM + wg * 32;
+    const int rows = max(0, min(32, Sq - row0));
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(qbh + (size_t)row0 * D), (short)0, rows * D * 2, kRsrcWord3);
+#pragma unroll
+    for (int ii = 0; ii < C::QI; ++ii) {
+      const int P = 64 * ii + lane;
+      const int row = P / C::CH, pc = P % C::CH;
+      const int voffs = (row * D + ((pc ^ swz_k<D>(row)) << 3)) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(sQ + (wg * 32) * D + 64 * ii * 8), 16, voffs, 0, 0,
+                                               0);
+    }
+  };
+  auto load_q_lds = [&]() __attribute__((always_inline)) {
+    const int row = wg * 32 + ln;
+    const char* base = (const char*)sQ + row * (D * 2);
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      uint4 x = *(const uint4*)(base + (((2 * ks + hl) ^ swz_k<D>(row)) << 4));
+      x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
       qreg[ks] = __builtin_bit_cast(bf16x8, x);
     }
   };
@@ -226,7 +261,8 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   auto kread = [&](const char* kbase, int kr, int sw, int ks) __attribute__((always_inline)) {
     return *(const bf16x8*)(kbase + kr + (((2 * ks + hl) ^ sw) << 4));
   };
-  // V^T operand rows/columns (transpose reads): see the header comment.
+  // V^T operand (transpose reads): lane (group gg = lane/16, j = lane%16) reads
+  // 8 bytes of row (32 sub + 16 s + 4 hl + j/4 [+8]) at dims 32 db + 16 (gg%2) + 4 (j%4).
   const int gg = lane >> 4, jj = lane & 15, dh = gg & 1;
   auto vread = [&](const char* vbase, int sub, int s, int db) __attribute__((always_inline)) {
     const int row1 = 32 * sub + 16 * s + 4 * hl + (jj >> 2);
@@ -239,75 +275,108 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
 
-  // Online-softmax update from the tile max; returns the rescale factor.
-  auto update_max = [&](float mx) __attribute__((always_inline)) {
-    mx = pair_max(mx);
-    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
-    float alpha = 1.f;
-    if (cand > m_run + kTau) {
-      alpha = fast_exp2(m_run - cand);
-      m_run = cand;
+  // ---- slot state carried between slots
+  f32x16 S0 = f32x16{}, S1 = f32x16{};  // scores of the block in flight (M -> V slot)
+  bf16x8 P[2][2];                        // probabilities (V -> next M slot)
+  bool s_vis = false;                    // scores in S0/S1 belong to a block this wave sees
+  bool p_vis = false;                    // P holds a block to accumulate
+  int s_kv0 = 0, s_q0 = 0;               // key / query origin of the block in S0/S1
+
+  // MFMA slot k: PV of block k-1, tile switch if block k starts a new tile,
+  // then S of block k. (sKc: K stage of block k; sVp: V stage of block k-1;
+  // sKn, sVc: stages that receive K of block k+1 and V of block k.)
+  // It runs as one stream of 32 MFMAs - 16 of PV, then 16 of S - whose LDS
+  // operands are read kPF MFMAs ahead, so the matrix core does not wait on LDS
+  // latency. When no PV is pending its probabilities are zero (the V stage
+  // always holds finite data); when block k is not needed its scores are
+  // computed and dropped. Both cases are rare, and branch-free this way.
+  constexpr int kPV = 4 * C::DB;  // PV MFMAs: (sub, s, db)
+  constexpr int kS = 2 * C::KS;   // S MFMAs: (ks, sub)
+  constexpr int kPF = 4;          // operand prefetch distance (MFMAs)
+  auto mslot = [&](int k, const __bf16* sKc, const __bf16* sVp, __bf16* sKn, __bf16* sVc) __attribute__((always_inline)) {
+    const char* vbase = (const char*)(sVp + grp * C::ELEMS);
+    const char* kbase = (const char*)(sKc + grp * C::ELEMS);
+    if (!p_vis) {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      P[0][0] = P[0][1] = P[1][0] = P[1][1] = __builtin_bit_cast(bf16x8, z);
     }
-    return alpha;
-  };
-  auto rescale = [&](float alpha, float lsum) __attribute__((always_inline)) {
-    l_run = alpha * l_run + lsum;
-    if (__any(alpha != 1.f)) {
+    S0 = f32x16{};
+    S1 = f32x16{};
+    // operand of MFMA number i of the stream
+    auto opnd = [&](int i) __attribute__((always_inline)) {
+      if (i < kPV) return vread(vbase, i / (2 * C::DB), (i / C::DB) & 1, i % C::DB);
+      const int j = i - kPV;
+      return kread(kbase, (j & 1) ? kr1 : kr0, (j & 1) ? sw1 : sw0, j >> 1);
+    };
+    bf16x8 buf[kPF];
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int i = 0; i < kPF; ++i) buf[i] = opnd(i);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+    for (int i = 0; i < kPV + kS; ++i) {
+      const bf16x8 a = buf[i % kPF];
+      if (i + kPF < kPV + kS) buf[i % kPF] = opnd(i + kPF);
+      if (i + kPF == kPV) {
+        // all V reads of this slot are issued: start the loads for later slots
+        __builtin_amdgcn_sched_barrier(0);
+        if (k + 1 < cnt) dma(kbh, sKn, koff, kv_of(k + 1));
+        if (k < cnt) dma(vbh, sVc, voff, kv_of(k));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i < kPV) {
+        const int sub = i / (2 * C::DB), ss = (i / C::DB) & 1, db = i % C::DB;
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[sub][ss], O[db], 0, 0, 0);
+      } else {
+        const int j = i - kPV;
+        if (j & 1)
+          S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[j >> 1], S1, 0, 0, 0);
+        else
+          S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[j >> 1], S0, 0, 0, 0);
+      }
+      // keep this order: the scheduler would otherwise sink each read next to
+      // its MFMA and the matrix core would wait out the LDS latency every time
+      __builtin_amdgcn_sched_barrier(0);
     }
-  };
-  // exp2, row-sum and bf16 packing of one 32-key sub-tile. Masked scores are
-  // -inf and come out as exactly 0 (c > 0 and mu finite).
-  auto probs = [&](const f32x16& Ssub, float mu, bf16x8* P2, float& la, float& lb) __attribute__((always_inline)) {
-    float e[16];
+    p_vis = false;
+    s_vis = false;
+    if (k >= cnt) return;
+    const int t = tile_of(k);
+    if (t != cur_tile) {
+      // group A moving from t0 to t1 (Q of t1 staged in LDS): the scores above
+      // used t0's Q; finish t0, then redo S with t1's Q.
+      store_tile(cur_tile);
+      // Let the stores drain here, once, so that no store is still reading its
+      // data registers when the loop reuses them.
+      wait_dma();
+      reset_state();
+      load_q_lds();
+      cur_tile = t;
+      S0 = f32x16{};
+      S1 = f32x16{};
 #pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(Ssub[r], c, -mu));
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) { la += e[r]; lb += e[r + 1]; }
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 w;
-      w.x = pack_bf16x2(e[8 * s + 0], e[8 * s + 1]);
-      w.y = pack_bf16x2(e[8 * s + 2], e[8 * s + 3]);
-      w.z = pack_bf16x2(e[8 * s + 4], e[8 * s + 5]);
-      w.w = pack_bf16x2(e[8 * s + 6], e[8 * s + 7]);
-      P2[s] = __builtin_bit_cast(bf16x8, w);
-    }
-  };
-  auto pv = [&](const char* vbase, int sub, const bf16x8* P2) __attribute__((always_inline)) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 a = vread(vbase, sub, s, 0);
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        bf16x8 an = a;
-        if (db + 1 < C::DB) an = vread(vbase, sub, s, db + 1);
-        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P2[s], O[db], 0, 0, 0);
-        a = an;
+      for (int ks = 0; ks < C::KS; ++ks) {
+        S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kbase, kr0, sw0, ks), qreg[ks], S0, 0, 0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kbase, kr1, sw1, ks), qreg[ks], S1, 0, 0, 0);
       }
     }
+    const int q0 = t * kBM + wg * 32;
+    const int kv0 = kv_of(k) * kBN;
+    s_vis = kv0 < Skv && (!causal || kv0 <= q0 + 31 + off);
+    s_kv0 = kv0;
+    s_q0 = q0;
   };
 
-  // One 64-key block for this wave's 32 rows. Blocks that some row sees only
-  // partly (causal diagonal, end of the keys) get their invisible scores set to
-  // -inf behind a wave-uniform branch; a block no row of the wave sees is skipped.
-  auto block = [&](const __bf16* sK, const __bf16* sV, int q0, int kv0) __attribute__((always_inline)) {
-    if (kv0 >= Skv || (causal && kv0 > q0 + 31 + off)) return;
-    const char* kbase = (const char*)(sK + grp * C::ELEMS);
-    const char* vbase = (const char*)(sV + grp * C::ELEMS);
-    f32x16 S0 = f32x16{}, S1 = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      const bf16x8 a0 = kread(kbase, kr0, sw0, ks);
-      const bf16x8 a1 = kread(kbase, kr1, sw1, ks);
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qreg[ks], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qreg[ks], S1, 0, 0, 0);
-    }
+  // Vector slot: softmax of the block in S0/S1 -> P, with the online update.
+  auto vslot = [&]() __attribute__((always_inline)) {
+    if (!s_vis) return;
+    const int kv0 = s_kv0, q0 = s_q0;
     const bool full = kv0 + kBN <= Skv && (!causal || kv0 + kBN - 1 <= q0 + off);
-    if (!full) {
+    float mx;
+    if (full) {
+      mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+    } else {
       // key of register r of sub-tile u is kb + 8*(r/4) + (r%4), kb = kv0 + 32u + 4hl;
       // visible iff < Skv and (non-causal or) <= query row + off
       const int kb = kv0 + 4 * hl;
@@ -319,72 +388,113 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
         if (ko > lim) S0[r] = -INFINITY;
         if (ko + 32 > lim) S1[r] = -INFINITY;
       }
-    }
-    float mx = fmaxf(S0[0], S1[0]);
+      mx = -INFINITY;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-    const float alpha = update_max(mx);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+    }
+    mx = pair_max(mx);
+    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+    float alpha = 1.f;
+    if (cand > m_run + kTau) {
+      alpha = fast_exp2(m_run - cand);
+      m_run = cand;
+    }
     const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-    bf16x8 P0[2], P1[2];
+    // Masked scores are -inf: with c > 0 and mu finite their exp2 is exactly 0.
+    // The row sum adds the bf16-rounded probabilities two at a time with
+    // v_dot2_f32_bf16 against (1, 1): the same values the PV product uses.
+    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
     float la = 0.f, lb = 0.f;
-    probs(S0, mu, P0, la, lb);
-    probs(S1, mu, P1, la, lb);
-    rescale(alpha, la + lb);
-    pv(vbase, 0, P0);
-    pv(vbase, 1, P1);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(sub ? S1[r] : S0[r], c, -mu));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        uint4 w;
+        w.x = pack_bf16x2(e[8 * s + 0], e[8 * s + 1]);
+        w.y = pack_bf16x2(e[8 * s + 2], e[8 * s + 3]);
+        w.z = pack_bf16x2(e[8 * s + 4], e[8 * s + 5]);
+        w.w = pack_bf16x2(e[8 * s + 6], e[8 * s + 7]);
+        P[sub][s] = __builtin_bit_cast(bf16x8, w);
+        la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), ones, la, false);
+        lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), ones, lb, false);
+        la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), ones, la, false);
+        lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), ones, lb, false);
+      }
+    }
+    l_run = alpha * l_run + (la + lb);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+    }
+    p_vis = true;
   };
 
-  // One iteration: barrier, prefetch the next block into the other stage,
-  // consume this block. (sKc, sVc) is this iteration's stage.
-  auto body = [&](int i, int t, __bf16* sKc, __bf16* sVc, __bf16* sKn, __bf16* sVn) __attribute__((always_inline)) {
-    __syncthreads();
-    if (i + 1 < cnt) dma(sKn, sVn, kv_of(i + 1));
-    block(sKc, sVc, t * kBM + wg * 32, kv_of(i) * kBN);
-  };
-  // Iterations [i0, i1) of this group, all on tile t; the stage is the
-  // iteration's parity (the loop walks aligned pairs and skips iterations
-  // outside the range, so each stage's code appears once).
-  auto run = [&](int i0, int i1, int t) __attribute__((always_inline)) {
-    for (int i = i0 & ~1; i < i1; i += 2) {
-      if (i >= i0) body(i, t, sK0, sV0, sK1, sV1);
-      if (i + 1 < i1) body(i + 1, t, sK1, sV1, sK0, sV0);
-    }
-  };
-
-  // ---- main loops: both groups execute exactly maxcnt barriers.
-  // Group A: phase 0 = all of t0, phase 1 = the tail of t1's KV range.
-  // Group B: phase 0 = the head of t1's KV range.
-  if (cnt > 0) dma(sK0, sV0, kv_of(0));
-  for (int phase = 0; phase < 2; ++phase) {
-    int i0, i1, t;
-    if (grp == 0) {
-      i0 = phase ? nA0 : 0;
-      i1 = phase ? cntA : nA0;
-      t = phase ? t1 : t0;
-    } else {
-      i0 = 0;
-      i1 = phase ? 0 : cntB;
-      t = t1;
-    }
-    if (i0 >= i1) continue;
-    reset_state();
-    load_q(t);
-    run(i0, i1, t);
-    if (grp == 0 && phase == 0) store_tile(t0);
+  // ---- prologue: zero this group's V slot of stage 1 (the first MFMA slot
+  // reads it with zero probabilities), first K block and first Q tile of each
+  // group, group A's second Q tile.
+  {
+    uint4* z = (uint4*)(sV1 + grp * C::ELEMS) + wg * (C::ELEMS / 8 / 4);
+#pragma unroll
+    for (int i = 0; i < C::ELEMS / 8 / 4 / 64; ++i) z[i * 64 + lane] = make_uint4(0, 0, 0, 0);
   }
-  for (int i = cnt; i < maxcnt; ++i) __syncthreads();
+  if (cnt > 0) {
+    dma(kbh, sK0, koff, kv_of(0));
+    cur_tile = tile_of(0);
+    reset_state();
+    load_q_global(cur_tile);
+  }
+  if (grp == 0 && cntA > nA0 && nA0 > 0) stage_q(t1);
+
+  // ---- slots. Every wave runs the same sequence M(0) V(0) M(1) V(1) ...,
+  // one barrier per slot; group B takes one empty slot first, so its MFMA slots
+  // line up with group A's vector slots. Unrolled by 2 blocks so that every LDS
+  // stage is a compile-time choice (stage of block k = k & 1). Both groups then
+  // pad to the same number of barriers.
+  int nbar = 0;
+  if (grp == 1) {
+    lds_barrier();
+    ++nbar;
+  }
+  for (int k = 0; k <= cnt; k += 2) {
+    wait_dma();
+    lds_barrier();
+    mslot(k, sK0, sV1, sK1, sV0);
+    lds_barrier();
+    if (k < cnt) vslot();
+    wait_dma();
+    lds_barrier();
+    if (k + 1 <= cnt) mslot(k + 1, sK1, sV0, sK0, sV1);
+    lds_barrier();
+    if (k + 1 < cnt) vslot();
+    nbar += 4;
+  }
+  {
+    const int nbA = 4 * (cntA / 2 + 1), nbB = 1 + 4 * (cntB / 2 + 1);
+    const int total = max(nbA, nbB);
+    for (; nbar < total; ++nbar) lds_barrier();
+  }
 
   // ---- epilogue: group A hands its partial of t1 to group B through LDS.
+  wait_dma();
   __syncthreads();
   float* xo = (float*)((wg < 2 ? (char*)sK0 : (char*)sV0)) + (wg & 1) * C::XO;
   float* xml = (float*)sK1 + wg * 128;
-  if (grp == 0 && split) {
+  if (grp == 0) {
+    if (split) {
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
+      for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = O[db][r];
-    xml[lane * 2 + 0] = m_run;
-    xml[lane * 2 + 1] = l_run;
+        for (int r = 0; r < 16; ++r) xo[(db * 16 + r) * 64 + lane] = O[db][r];
+      xml[lane * 2 + 0] = m_run;
+      xml[lane * 2 + 1] = l_run;
+    } else if (cur_tile >= 0) {
+      store_tile(cur_tile);
+    }
   }
   __syncthreads();
   if (grp == 1) {
@@ -407,7 +517,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
-  dim3 grid(p.nP, p.Hq, p.B), block(512);
+  dim3 grid(p.nP * p.Hq * p.B), block(512);
   if (d == 128)
     hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, p);
   else
