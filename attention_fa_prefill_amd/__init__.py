@@ -22,8 +22,8 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
-EXPORTS = ("fa_status_string", "fa_version", "fa_prefill", "fa_prefill_f32", "fa_decode_workspace_bytes",
-           "fa_decode", "fa_merge_lse")
+EXPORTS = ("fa_status_string", "fa_version", "fa_prefill", "fa_prefill_f32", "fa_decode_split_tokens",
+           "fa_decode_workspace_bytes", "fa_decode", "fa_merge_lse")
 
 _lib = None
 
@@ -51,7 +51,9 @@ def lib() -> ctypes.CDLL:
         L.fa_prefill.restype = ci
         L.fa_prefill_f32.argtypes = pre
         L.fa_prefill_f32.restype = ci
-        L.fa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci]
+        L.fa_decode_split_tokens.argtypes = [ci, ci, ci, ci, ci]
+        L.fa_decode_split_tokens.restype = ci
+        L.fa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
         L.fa_decode_workspace_bytes.restype = sz
         L.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, sz, vp]
         L.fa_decode.restype = ci
@@ -134,8 +136,13 @@ def prefill(q, k, v, o=None, *, causal: bool = True, scale: float | None = None,
     return o
 
 
-def decode_workspace_bytes(B: int, Hq: int, d: int, max_kv_len: int, tokens_per_split: int = 0) -> int:
-    return int(lib().fa_decode_workspace_bytes(B, Hq, d, max_kv_len, tokens_per_split))
+def decode_split_tokens(B: int, Hq: int, Hkv: int, max_kv_len: int, tokens_per_split: int = 0) -> int:
+    """KV tokens per split that fa_decode uses for these sizes (0 if invalid)."""
+    return int(lib().fa_decode_split_tokens(B, Hq, Hkv, max_kv_len, tokens_per_split))
+
+
+def decode_workspace_bytes(B: int, Hq: int, Hkv: int, d: int, max_kv_len: int, tokens_per_split: int = 0) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, Hq, Hkv, d, max_kv_len, tokens_per_split))
 
 
 def decode(q, kcache, vcache, seqlens, *, block_table=None, max_kv_len: int | None = None, scale: float | None = None,
@@ -174,7 +181,7 @@ def decode(q, kcache, vcache, seqlens, *, block_table=None, max_kv_len: int | No
         scale = 1.0 / math.sqrt(d)
     if o is None:
         o = torch.empty_like(q)
-    need = decode_workspace_bytes(B, Hq, d, mkl, tokens_per_split)
+    need = decode_workspace_bytes(B, Hq, Hkv, d, mkl, tokens_per_split)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     check(lib().fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens), _ptr(o), B, Hq,

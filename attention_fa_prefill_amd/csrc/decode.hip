@@ -10,25 +10,27 @@
 //
 // Split kernel: one work-group (4 waves) per (sequence b, kv head g, group of
 // up to 16 query heads sharing g, split s of tps tokens). Waves take 32-token
-// steps round-robin. Per step:
+// steps round-robin and keep two steps of loads in flight. Per step:
 //   - K rows go HBM -> VGPRs directly in the A-operand layout of
 //     v_mfma_f32_16x16x32_bf16 (16 tokens x 32 dims per MFMA);
+//   - V rows go HBM -> the wave's LDS stage with direct-to-LDS buffer loads
+//     (16 bytes per lane, swizzled), and come back through ds_read_b64_tr_b16
+//     as the A operand of O^T += V^T . P^T;
 //   - S^T = K . Q^T for all query heads of the group at once (Q^T lives in
 //     VGPRs; unused head columns are zero), so the FLOPs ride on MFMA and the
 //     vector ALU only runs the softmax;
-//   - V rows go HBM -> VGPRs -> the wave's own LDS slot, then come back through
-//     ds_read_b64_tr_b16 as the A operand of O^T += V^T . P^T;
 //   - online softmax per head with a lazily raised running max.
-// The next step's K and V loads are issued before the current step is used.
-// Tokens past the sequence length get score -inf and a zero V row (never a NaN
-// times zero); block-table entries past the last page are never read.
+// Every load goes through a buffer resource whose record count ends at the
+// last valid token row of its page, so rows past the sequence length (and the
+// slack of the last page) read as zero without touching memory; their scores
+// are set to -inf. Block-table entries past the last page are never read.
 // At the end the 4 waves' states are merged in LDS and the split writes its
 // normalised output and natural-log log-sum-exp to the workspace.
 //
 // Paged and contiguous caches run the same instructions in the same order and
 // differ only in the row address, so their results are bitwise equal.
 //
-// Merge kernel: per (row, 32 output dims), M = max lse_s, w_s = exp(lse_s - M),
+// Merge kernel: per row, M = max lse_s, w_s = exp(lse_s - M),
 // o = sum_s w_s o_s / sum_s w_s, lse = M + log(sum_s w_s); empty splits skipped.
 #include "fa_internal.h"
 
@@ -40,28 +42,49 @@ constexpr float kTau = 8.0f;   // lazy rescale threshold (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
-}
-
 // V staging swizzle: 16-byte chunk XOR 2*(row % 8) (D=128) / 2*(row % 4) (D=64),
 // so the 4-row x 32-byte footprint of each transpose read hits distinct banks.
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return 2 * (row & (D == 128 ? 7 : 3)); }
+
+// Waits for this wave's vector-memory loads (direct-to-LDS included) until at
+// most N are outstanding. The memory clobber keeps LDS reads of a stage from
+// being scheduled above the wait that covers that stage's loads.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N == 0 || N == 8 || N == 16, "wait count");
+  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kMaxPages = 128;           // pages per split (tps <= 2048)
+constexpr int kPageSlots = kMaxPages + 32;  // + the pages of the loads issued past the end
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 
 template <int D>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   constexpr int KS = D / 32;         // k-steps of S^T = K . Q^T (16x16x32)
   constexpr int DB = D / 16;         // 16-dim blocks of O^T
   constexpr int CH = D / 8;          // 16-byte chunks per row
-  constexpr int VL = kStep * CH / 64;  // V chunk loads per lane per step
-  constexpr int MAXP = 64;           // block-table entries cached per split (tps <= 1024)
-  __shared__ __attribute__((aligned(16))) __bf16 sV[4][kStep * D];
+  constexpr int RI = 64 / CH;        // V rows per direct-to-LDS load (4 for D=128)
+  constexpr int VDMA = kStep / RI;   // direct-to-LDS loads per step
+  constexpr int NLD = 2 * KS + VDMA; // vector-memory instructions issued per step
+  // Two V stages per wave (the step being used and the one in flight).
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[4][kStep * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[4][kStep * D];
   __shared__ float sM[4][64], sL[4][64];
-  __shared__ int sRow0[MAXP];        // first cache row of each page of this split
+  __shared__ int sRow0[kPageSlots];  // first cache row of each page of this split
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x;
   const int g = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;
   const int b = blockIdx.z;
@@ -75,15 +98,18 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   const int nh = min(16, p.G - hc * 16);
   const int Hkv = p.Hkv;
 
-  // First cache row of each 16-token page this split touches.
+  // Pages past the end of the sequence get row 0: their loads have a zero
+  // record count and never touch memory.
   const int npg = (tok1 - tok0 + 15) / 16;
-  for (int i = tid; i < npg; i += 256) {
+  for (int i = tid; i < kPageSlots; i += 256) {
     const int pg = tok0 / 16 + i;
-    sRow0[i] = p.bt ? p.bt[(size_t)b * p.pages_per_seq + pg] * 16 : b * p.max_len + pg * 16;
+    int row0 = 0;
+    if (i < npg) row0 = p.bt ? p.bt[(size_t)b * p.pages_per_seq + pg] * 16 : b * p.max_len + pg * 16;
+    sRow0[i] = row0;
   }
   __syncthreads();
 
-  const int n = lane & 15, cq = lane >> 4;  // MFMA column (head) and k-group
+  const int n = lane & 15, cq = lane >> 4;  // MFMA column (head / token) and k-group
   // Q^T operand: lane holds q[b, hq0+n, 32 ks + 8 cq .. +8]; zero columns past nh.
   bf16x8 qop[KS];
   {
@@ -97,35 +123,39 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
     }
   }
 
-  const __bf16* kc = (const __bf16*)p.kc;
-  const __bf16* vc = (const __bf16*)p.vc;
-  auto row_of = [&](int tok) { return (size_t)(sRow0[(tok - tok0) >> 4] + (tok & 15)); };
-
-  // K operand registers for one step: [half][ks], token = tb + 16 half + n.
-  bf16x8 kreg[2][KS];
-  uint4 vreg[VL];
-  auto load_step = [&](int st) {
-    const int tb = tok0 + st * kStep;
+  // Buffer resource over page pi (relative to the split) of kv head g: its
+  // record count ends right after the last valid token row, so rows past the
+  // sequence length read as zero (K: masked score; V: no NaN can leak).
+  const size_t rowstride = (size_t)Hkv * D * 2;  // bytes between consecutive tokens
+  auto page_rsrc = [&](const void* cache, int pi) __attribute__((always_inline)) {
+    const int nvalid = max(0, min(16, tok1 - (tok0 + 16 * pi)));
+    const int row0 = __builtin_amdgcn_readfirstlane(sRow0[pi]);
+    const char* base = (const char*)cache + ((size_t)row0 * Hkv + g) * (size_t)(D * 2);
+    const int nrec = max(0, (nvalid - 1) * (int)rowstride + D * 2);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kRsrcWord3);
+  };
+  // K operand of one 32-token step: half h = page 2st+h, lane (n, cq) holds
+  // K[token n of the page][32 ks + 8 cq .. +8] - the A layout of 16x16x32.
+  const int koff = (int)((size_t)n * rowstride) + 16 * cq;
+  auto load_k = [&](int st, u32x4 (&kb)[2][KS]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tok = tb + 16 * half + n;
-      const bool ok = tok < tok1;
-      const __bf16* src = kc + (row_of(ok ? tok : tb) * Hkv + g) * D + 8 * cq;
+    for (int h = 0; h < 2; ++h) {
+      const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.kc, 2 * st + h);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (ok) x = *(const uint4*)(src + 32 * ks);
-        kreg[half][ks] = __builtin_bit_cast(bf16x8, x);
-      }
+      for (int ks = 0; ks < KS; ++ks)
+        kb[h][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff + 64 * ks, 0, 0);
     }
+  };
+  // V rows of one step -> this wave's LDS stage, 16 bytes per lane per load;
+  // LDS chunk pc of row r holds logical chunk pc ^ swz(r).
+  auto dma_v = [&](int st, __bf16* stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ii = 0; ii < VL; ++ii) {
-      const int P = 64 * ii + lane;
-      const int r = P / CH, ch = P % CH;
-      const int tok = tb + r;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (tok < tok1) x = *(const uint4*)(vc + (row_of(tok) * Hkv + g) * D + ch * 8);
-      vreg[ii] = x;
+    for (int ii = 0; ii < VDMA; ++ii) {
+      const int r = ii * RI + lane / CH, pc = lane % CH;
+      const int h = (ii * RI) / 16;  // page of this load (uniform)
+      const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.vc, 2 * st + h);
+      const int voff = (int)((size_t)(r & 15) * rowstride) + ((pc ^ swz_v<D>(r)) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + ii * 64 * 8), 16, voff, 0, 0, 0);
     }
   };
 
@@ -134,45 +164,31 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   for (int db = 0; db < DB; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.c;
-  char* vslot = (char*)sV[w];
+  const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
+  const int y = lane & 15;
+  const int row1 = 4 * cq + (y >> 2), row2 = 16 + 4 * cq + (y >> 2);
 
-  int st = w;
-  if (st < nsteps) load_step(st);
-  for (; st < nsteps; st += 4) {
+  // One 32-token step from K registers kb and V stage `stage`.
+  auto step = [&](int st, const u32x4 (&kb)[2][KS], const __bf16* stage) __attribute__((always_inline)) {
     const int tb = tok0 + st * kStep;
-    // S^T = K . Q^T for the two 16-token halves
     f32x4 S[2];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      S[half] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int h = 0; h < 2; ++h) {
+      S[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        S[half] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[half][ks], qop[ks], S[half], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) S[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[h][ks]), qop[ks], S[h], 0, 0, 0);
     }
-    // stage V into this wave's LDS slot (swizzled)
+    // S^T lane (n, cq) reg r is token tb + 16 h + 4 cq + r of head n; tokens
+    // past the end get -inf (their K rows read as zero).
+    if (tb + kStep > tok1) {
 #pragma unroll
-    for (int ii = 0; ii < VL; ++ii) {
-      const int P = 64 * ii + lane;
-      const int r = P / CH, ch = P % CH;
-      *(uint4*)(vslot + r * (D * 2) + ((ch ^ swz_v<D>(r)) << 4)) = vreg[ii];
-    }
-    // prefetch the next step of this wave
-    if (st + 4 < nsteps) load_step(st + 4);
-
-    // mask tokens past the end: S^T lane (n, cq) reg r is token tb + 16 half + 4 cq + r
-    const bool tail = tb + kStep > tok1;
-    if (tail) {
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (tb + 16 * half + 4 * cq + r >= tok1) S[half][r] = -INFINITY;
+          if (tb + 16 * h + 4 * cq + r >= tok1) S[h][r] = -INFINITY;
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[half][r]);
+    float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                     fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
@@ -182,37 +198,26 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
       m_run = cand;
     }
     const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-    float e[8];
-    float lsum = 0.f;
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float x = fast_exp2(fmaf(S[half][r], c, -mu));
-        if (tail && S[half][r] == -INFINITY) x = 0.f;
-        e[4 * half + r] = x;
-        lsum += x;
-      }
-    l_run = alpha * l_run + lsum;
+    // masked scores are -inf and c > 0: their exp2 is exactly 0
+    uint4 pw;
+    pw.x = pack2(fast_exp2(fmaf(S[0][0], c, -mu)), fast_exp2(fmaf(S[0][1], c, -mu)));
+    pw.y = pack2(fast_exp2(fmaf(S[0][2], c, -mu)), fast_exp2(fmaf(S[0][3], c, -mu)));
+    pw.z = pack2(fast_exp2(fmaf(S[1][0], c, -mu)), fast_exp2(fmaf(S[1][1], c, -mu)));
+    pw.w = pack2(fast_exp2(fmaf(S[1][2], c, -mu)), fast_exp2(fmaf(S[1][3], c, -mu)));
+    // row sum of the bf16-rounded probabilities (the values PV uses)
+    float la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.x), ones, 0.f, false);
+    la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.y), ones, la, false);
+    float lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.z), ones, 0.f, false);
+    lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw.w), ones, lb, false);
+    l_run = alpha * l_run + (la + lb);
     if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) O[db] *= alpha;
     }
-    uint4 pw;
-    pw.x = pack_bf16x2(e[0], e[1]);
-    pw.y = pack_bf16x2(e[2], e[3]);
-    pw.z = pack_bf16x2(e[4], e[5]);
-    pw.w = pack_bf16x2(e[6], e[7]);
     const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-
-    // the slot was written by this wave only: order its writes before the reads
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // O^T += V^T . P^T; contraction index 8 cq + i is token 4 cq + i (i < 4)
     // or 16 + 4 cq + (i - 4) (i >= 4), matching the score registers.
-    const int y = lane & 15;
-    const int row1 = 4 * cq + (y >> 2), row2 = 16 + 4 * cq + (y >> 2);
+    const char* vslot = (const char*)stage;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int colb = (16 * db + 4 * (y & 3)) * 2;
@@ -223,14 +228,39 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pop, O[db], 0, 0, 0);
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // Waves take steps w, w+4, w+8, ...; each wave keeps two steps in flight:
+  // K in two register buffers, V in two LDS stages. Every load call issues
+  // exactly NLD instructions (those of steps past the end read nothing), so
+  // the outstanding-load count at each wait is the same on every path.
+  const int nw = nsteps > w ? (nsteps - w + 3) / 4 : 0;
+  // kept as raw dwords: a bf16-typed copy across the loop makes the compiler
+  // repack the halves, which waits for the loads right after they are issued
+  u32x4 kA[2][KS], kB[2][KS];
+  __bf16* stA = sV0[w];
+  __bf16* stB = sV1[w];
+  dma_v(w, stA);
+  load_k(w, kA);
+  dma_v(w + 4, stB);
+  load_k(w + 4, kB);
+  for (int i = 0; i < nw; i += 2) {
+    wait_vm<NLD>();  // step i's loads are done; step i+1's may be pending
+    step(w + 4 * i, kA, stA);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's reads of stage A are done
+    dma_v(w + 4 * (i + 2), stA);
+    load_k(w + 4 * (i + 2), kA);
+    wait_vm<NLD>();
+    if (i + 1 < nw) step(w + 4 * (i + 1), kB, stB);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    dma_v(w + 4 * (i + 3), stB);
+    load_k(w + 4 * (i + 3), kB);
   }
+  wait_vm<0>();  // no direct-to-LDS write may land after the stages are reused
 
   // ---- merge the 4 waves: O^T lane (n, cq) reg r is dim 16 db + 4 cq + r of head n.
   __syncthreads();
-  float* xo = (float*)sV[w];
+  float* xo = (float*)sV0[w];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -259,30 +289,34 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
     float* dst = p.ws_o + (((size_t)b * p.Hq + hq) * p.nsplit + s) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
-      float4 v;
       float acc[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float x = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x += a[u] * ((const float*)sV[u])[(db * 4 + r) * 64 + lane];
+        for (int u = 0; u < 4; ++u) x += a[u] * ((const float*)sV0[u])[(db * 4 + r) * 64 + lane];
         acc[r] = x * inv;
       }
-      v = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      *(float4*)(dst + 16 * db + 4 * cq) = v;
+      *(float4*)(dst + 16 * db + 4 * cq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
-    if (cq == 0) p.ws_lse[((size_t)b * p.Hq + hq) * p.nsplit + s] = (M + __log2f(L)) * kLn2;
+    if (cq == 0) p.ws_lse[((size_t)b * p.Hq + hq) * p.nsplit + s] = (M + log2f(L)) * kLn2;
   }
 }
 
-// Merge: grid (R, D/32), 256 threads = 32 dims x 8 split groups.
-__global__ void __launch_bounds__(256) merge_kernel(MergeParams p, int D) {
-  __shared__ float red[256];
-  __shared__ float acc_s[8][32];
-  const int tid = threadIdx.x;
+// Merge: one work-group of 256 threads per output row. M = max of the row's
+// log-sum-exps (wave shuffles, then LDS across the 4 waves); then D/4 threads
+// per split read 16 bytes each, so one split's row is one coalesced access,
+// and 256/(D/4) split groups stride over the splits, 4 splits per round.
+// Splits whose lse is -inf carry no weight and their partial output is ignored.
+template <int D>
+__global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
+  constexpr int TPR = D / 4;     // threads per split row
+  constexpr int NG = 256 / TPR;  // split groups
+  __shared__ float red[4];
+  __shared__ float4 accs[NG][TPR];
+  __shared__ float wsum_s[NG];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r = blockIdx.x;
-  const int d = blockIdx.y * 32 + (tid & 31);
-  const int sg = tid >> 5;
   int nS = p.S;
   if (p.lens) {
     int len = p.lens[r / p.Hq];
@@ -292,40 +326,65 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p, int D) {
   const float* lse = p.lse + (size_t)r * p.S;
   float M = -INFINITY;
   for (int s = tid; s < nS; s += 256) M = fmaxf(M, lse[s]);
-  red[tid] = M;
-  __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
-  float acc = 0.f, W = 0.f;
-  if (M != -INFINITY) {
-    for (int s = sg; s < nS; s += 8) {
-      const float ls = lse[s];
-      if (ls == -INFINITY) continue;
-      const float wgt = expf(ls - M);
-      W += wgt;
-      acc += wgt * p.o_parts[((size_t)r * p.S + s) * D + d];
-    }
-  }
-  acc_s[sg][tid & 31] = acc;
-  red[tid] = W;
-  __syncthreads();
-  if (sg == 0) {
-    float a = 0.f, wsum = 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      a += acc_s[u][tid];
-      wsum += red[u * 32 + tid];
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if (lane == 0) red[w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  const int c = tid % TPR, sg = tid / TPR;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float W = 0.f;
+  if (M != -INFINITY) {
+    const float* op = p.o_parts + (size_t)r * p.S * D + 4 * c;
+    auto add = [&](float l, float4 x) __attribute__((always_inline)) {
+      const bool live = l != -INFINITY;
+      const float wt = live ? expf(l - M) : 0.f;
+      W += wt;
+      if (live) {
+        acc.x = fmaf(wt, x.x, acc.x);
+        acc.y = fmaf(wt, x.y, acc.y);
+        acc.z = fmaf(wt, x.z, acc.z);
+        acc.w = fmaf(wt, x.w, acc.w);
+      }
+    };
+    int s = sg;
+    for (; s + 3 * NG < nS; s += 4 * NG) {
+      float l[4];
+      float4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        l[u] = lse[s + u * NG];
+        x[u] = *(const float4*)(op + (size_t)(s + u * NG) * D);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) add(l[u], x[u]);
     }
-    const float val = (M == -INFINITY) ? 0.f : a / wsum;
-    if (p.out_bf16)
-      ((__bf16*)p.o)[(size_t)r * D + d] = (__bf16)val;
-    else
-      ((float*)p.o)[(size_t)r * D + d] = val;
-    if (p.lse_out && blockIdx.y == 0 && tid == 0) p.lse_out[r] = (M == -INFINITY) ? -INFINITY : M + logf(wsum);
+    for (; s < nS; s += NG) add(lse[s], *(const float4*)(op + (size_t)s * D));
+  }
+  accs[sg][c] = acc;
+  if (c == 0) wsum_s[sg] = W;
+  __syncthreads();
+  if (tid < TPR) {
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float wsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < NG; ++u) {
+      const float4 x = accs[u][tid];
+      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+      wsum += wsum_s[u];
+    }
+    const bool empty = M == -INFINITY;
+    const float inv = empty ? 0.f : 1.0f / wsum;
+    const float v0 = a.x * inv, v1 = a.y * inv, v2 = a.z * inv, v3 = a.w * inv;
+    if (p.out_bf16) {
+      __bf16* dst = (__bf16*)p.o + (size_t)r * D + 4 * tid;
+      const uint2 pk = make_uint2(pack2(v0, v1), pack2(v2, v3));
+      *(uint2*)dst = pk;
+    } else {
+      *(float4*)((float*)p.o + (size_t)r * D + 4 * tid) = make_float4(v0, v1, v2, v3);
+    }
+    if (p.lse_out && tid == 0) p.lse_out[r] = empty ? -INFINITY : M + logf(wsum);
   }
 }
 
@@ -355,8 +414,11 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) 
 }
 
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream) {
-  dim3 grid(p.R, d / 32), block(256);
-  hipLaunchKernelGGL(merge_kernel, grid, block, 0, stream, p, d);
+  dim3 grid(p.R), block(256);
+  if (d == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -9,8 +9,10 @@
 
 namespace {
 
-constexpr int kDefaultTps = 512;
-constexpr int kMaxTps = 1024;
+constexpr int kMinDefaultTps = 64;
+constexpr int kMaxDefaultTps = 1024;
+constexpr int kTargetSplitGroups = 512;  // two resident split work-groups per CU
+constexpr int kMaxTps = 2048;
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -52,7 +54,21 @@ fa::PrefillParams make_prefill(const void* q, const void* k, const void* v, void
   return p;
 }
 
-int resolve_tps(int tps) { return tps == 0 ? kDefaultTps : tps; }
+// Work-groups one split of every sequence launches: B * Hkv * ceil(G / 16).
+long split_streams(int B, int Hq, int Hkv) { return (long)B * Hkv * ((Hq / Hkv + 15) / 16); }
+
+// tokens_per_split == 0: the smallest power of two >= 64 that keeps the grid
+// near kTargetSplitGroups work-groups, capped at 1024 (a 256k-token sequence
+// then still has 256 splits). Any other value is taken as given (validated by
+// the caller). Returns 0 for invalid sizes.
+int resolve_tps(int B, int Hq, int Hkv, int max_kv_len, int tps) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_kv_len <= 0 || Hq % Hkv != 0) return 0;
+  if (tps != 0) return tps;
+  const long want = ((long)max_kv_len * split_streams(B, Hq, Hkv) + kTargetSplitGroups - 1) / kTargetSplitGroups;
+  int t = kMinDefaultTps;
+  while (t < kMaxDefaultTps && t < want) t *= 2;
+  return t;
+}
 
 }  // namespace
 
@@ -72,7 +88,7 @@ const char* fa_status_string(fa_status s) {
   return "FA_ERR_UNKNOWN";
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 200; }
 
 fa_status fa_prefill(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq, int Skv,
                      int d, float scale, int causal, void* stream) {
@@ -90,9 +106,15 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o, i
   return from_hip(fa::launch_prefill_f32(p, d, scale, (hipStream_t)stream));
 }
 
-size_t fa_decode_workspace_bytes(int B, int Hq, int d, int max_kv_len, int tokens_per_split) {
-  const int tps = resolve_tps(tokens_per_split);
-  if (B <= 0 || Hq <= 0 || d <= 0 || max_kv_len <= 0 || tps <= 0) return 0;
+int fa_decode_split_tokens(int B, int Hq, int Hkv, int max_kv_len, int tokens_per_split) {
+  const int tps = resolve_tps(B, Hq, Hkv, max_kv_len, tokens_per_split);
+  if (tps <= 0 || tps % 32 != 0 || tps > kMaxTps) return 0;
+  return tps;
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, int tokens_per_split) {
+  const int tps = fa_decode_split_tokens(B, Hq, Hkv, max_kv_len, tokens_per_split);
+  if (d <= 0 || tps <= 0) return 0;
   const size_t nsplit = ((size_t)max_kv_len + tps - 1) / tps;
   const size_t rows = (size_t)B * Hq * nsplit;
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
@@ -106,8 +128,8 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (block_table && page_size != 16) return FA_ERR_UNSUPPORTED;
-  const int tps = resolve_tps(tokens_per_split);
-  if (tps <= 0 || tps % 32 != 0 || tps > kMaxTps) return FA_ERR_ARG;
+  const int tps = fa_decode_split_tokens(B, Hq, Hkv, max_kv_len, tokens_per_split);
+  if (tps <= 0) return FA_ERR_ARG;
   if (!isfinite(scale)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o)) return FA_ERR_ALIGN;
   if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
@@ -115,7 +137,7 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   const int hchunks = (G + 15) / 16;
   if (B > kMaxGridYZ || (long)Hkv * hchunks > kMaxGridYZ) return FA_ERR_SHAPE;
   if (!block_table && (size_t)B * (size_t)max_kv_len > (size_t)INT32_MAX) return FA_ERR_SHAPE;
-  const size_t need = fa_decode_workspace_bytes(B, Hq, d, max_kv_len, tps);
+  const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_kv_len, tps);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
 
@@ -127,7 +149,8 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   p.nsplit = (max_kv_len + tps - 1) / tps;
   p.G = G;
   p.hchunks = hchunks;
-  p.c = fabsf(scale) * fa::kLog2e;
+  // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0
+  p.c = fmaxf(fabsf(scale) * fa::kLog2e, 1e-30f);
   p.neg = scale < 0.f ? 1 : 0;
   const size_t rows = (size_t)B * Hq * p.nsplit;
   p.ws_o = (float*)workspace;

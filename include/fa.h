@@ -105,12 +105,24 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
                          float scale, int causal, void* stream);
 
 /*
+ * fa_decode_split_tokens - the KV tokens each split work-group of fa_decode
+ * covers (n_split = ceil(max_kv_len / result) splits per sequence).
+ * tokens_per_split == 0 asks for the default: the smallest power of two in
+ * [64, 1024] for which B * Hkv * ceil((Hq/Hkv)/16) * n_split stays near 512
+ * work-groups (two per compute unit), so long sequences are split finely
+ * enough to fill the GPU; 1024 keeps a 262144-token sequence at 256 splits.
+ * Any other value must be a positive multiple of 32, at most 2048, and is
+ * returned unchanged. Returns 0 for invalid arguments.
+ */
+int fa_decode_split_tokens(int B, int Hq, int Hkv, int max_kv_len, int tokens_per_split);
+
+/*
  * fa_decode_workspace_bytes - bytes of device workspace fa_decode needs:
  * fp32 partial outputs [B, Hq, n_split, d] and partial log-sum-exps
- * [B, Hq, n_split], n_split = ceil(max_kv_len / tokens_per_split).
- * tokens_per_split == 0 selects the default (512). Returns 0 for invalid sizes.
+ * [B, Hq, n_split], each rounded up to 256 bytes, with n_split as above.
+ * Returns 0 for invalid arguments.
  */
-size_t fa_decode_workspace_bytes(int B, int Hq, int d, int max_kv_len, int tokens_per_split);
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, int tokens_per_split);
 
 /*
  * fa_decode - one query token per sequence attending to all of its cached
@@ -128,8 +140,9 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int d, int max_kv_len, int token
  *   seqlens     : int32 [B] device array, tokens cached for each sequence,
  *                 clamped to [0, max_kv_len]; length 0 gives o = 0.
  *   page_size   : must be 16 when block_table != NULL (ignored otherwise).
- *   tokens_per_split : KV tokens per split work-group; 0 -> 512; otherwise a
- *                 positive multiple of 32.
+ *   tokens_per_split : KV tokens per split work-group; 0 -> the default of
+ *                 fa_decode_split_tokens; otherwise a positive multiple of 32,
+ *                 at most 2048.
  *   workspace   : device scratch of at least fa_decode_workspace_bytes(...)
  *                 bytes, 16-byte aligned; contents undefined after the call.
  *   d           : 64 or 128.  Hq / Hkv query heads share one kv head.

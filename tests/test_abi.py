@@ -36,7 +36,7 @@ def test_status_strings_and_version():
     for code, name in fa.STATUS_NAMES.items():
         assert fa.status_string(code).startswith(name)
     assert fa.status_string(99) == "FA_ERR_UNKNOWN"
-    assert fa.lib().fa_version() == 100
+    assert fa.lib().fa_version() == 200
 
 
 def prefill(fn="fa_prefill", q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, Sq=8, Skv=8, d=128, scale=0.125, causal=1):
@@ -59,7 +59,7 @@ def test_prefill_rejects(fn, kw, code):
 def decode(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, page=16, tps=0, scale=0.1,
            ws=A, wsb=None):
     if wsb is None:
-        wsb = fa.decode_workspace_bytes(B, Hq, d, L, tps) if B > 0 else 0
+        wsb = fa.decode_workspace_bytes(B, Hq, Hkv, d, L, tps) if B > 0 else 0
     return fa.lib().fa_decode(q, k, v, bt, lens, o, B, Hq, Hkv, d, L, page, tps, scale, ws, wsb, None)
 
 
@@ -68,7 +68,7 @@ def decode(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, p
     (dict(B=0, wsb=1 << 20), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(L=0, wsb=1 << 20), SHAPE),
     (dict(Hkv=0), SHAPE),
     (dict(d=80), UNSUP), (dict(bt=A, page=32), UNSUP), (dict(bt=A, page=8), UNSUP),
-    (dict(tps=48), ARG), (dict(tps=-32), ARG), (dict(tps=2048), ARG), (dict(scale=float("nan")), ARG),
+    (dict(tps=48), ARG), (dict(tps=-32), ARG), (dict(tps=4096), ARG), (dict(scale=float("nan")), ARG),
     (dict(q=A + 2), ALIGN), (dict(k=A + 8), ALIGN), (dict(o=A + 4), ALIGN), (dict(lens=A + 2), ALIGN),
     (dict(bt=A + 1), ALIGN), (dict(ws=A + 8), ALIGN),
     (dict(ws=None), WS), (dict(wsb=16), WS),
@@ -77,16 +77,39 @@ def test_decode_rejects(kw, code):
     assert decode(**kw) == code
 
 
+def test_decode_split_tokens():
+    # explicit sizes are returned unchanged, invalid ones give 0
+    assert fa.decode_split_tokens(4, 32, 8, 32768, 256) == 256
+    assert fa.decode_split_tokens(4, 32, 8, 32768, 2048) == 2048
+    for bad in (48, -32, 4096):
+        assert fa.decode_split_tokens(4, 32, 8, 32768, bad) == 0
+    assert fa.decode_split_tokens(4, 32, 6, 32768, 0) == 0  # Hq % Hkv != 0
+    assert fa.decode_split_tokens(0, 32, 8, 32768, 0) == 0
+    # default: smallest power of two in [64, 1024] with
+    # B * Hkv * ceil(G / 16) * ceil(max_kv_len / tps) <= 512 work-groups
+    for B, Hq, Hkv, L in [(4, 32, 8, 32768), (8, 32, 8, 16384), (1, 16, 2, 262144), (1, 8, 8, 1024),
+                          (1, 1, 1, 1), (2, 64, 2, 4096), (3, 40, 8, 777)]:
+        t = fa.decode_split_tokens(B, Hq, Hkv, L, 0)
+        streams = B * Hkv * (-(-(Hq // Hkv) // 16))
+        fits = [x for x in (64, 128, 256, 512, 1024) if streams * L <= 512 * x]
+        assert t == (fits[0] if fits else 1024), (B, Hq, Hkv, L, t)
+    # the long-context workload keeps at least 256 splits
+    t5 = fa.decode_split_tokens(1, 16, 2, 262144, 0)
+    assert -(-262144 // t5) >= 256
+
+
 def test_decode_workspace_bytes():
     # [B, Hq, nsplit, d] fp32 partials + [B, Hq, nsplit] fp32 lse, each rounded up to 256 bytes
     n = 32768 // 512
-    assert fa.decode_workspace_bytes(4, 32, 128, 32768, 0) == 4 * 32 * n * 128 * 4 + 4 * 32 * n * 4
-    assert fa.decode_workspace_bytes(4, 32, 128, 32768, 512) == fa.decode_workspace_bytes(4, 32, 128, 32768, 0)
-    assert fa.decode_workspace_bytes(1, 1, 64, 1, 32) == 256 + 256
-    assert fa.decode_workspace_bytes(0, 1, 64, 1, 32) == 0
-    n5 = 262144 // 512
-    assert n5 >= 256  # the long-context workload merges at least 256 splits
-    assert fa.decode_workspace_bytes(1, 16, 128, 262144, 0) == 16 * n5 * 128 * 4 + 16 * n5 * 4
+    assert fa.decode_workspace_bytes(4, 32, 8, 128, 32768, 512) == 4 * 32 * n * 128 * 4 + 4 * 32 * n * 4
+    t = fa.decode_split_tokens(4, 32, 8, 32768, 0)
+    n = -(-32768 // t)
+    assert fa.decode_workspace_bytes(4, 32, 8, 128, 32768, 0) == 4 * 32 * n * 128 * 4 + 4 * 32 * n * 4
+    assert fa.decode_workspace_bytes(1, 1, 1, 64, 1, 32) == 256 + 256
+    assert fa.decode_workspace_bytes(0, 1, 1, 64, 1, 32) == 0
+    assert fa.decode_workspace_bytes(1, 8, 3, 64, 64, 32) == 0
+    n5 = -(-262144 // fa.decode_split_tokens(1, 16, 2, 262144, 0))
+    assert fa.decode_workspace_bytes(1, 16, 2, 128, 262144, 0) == 16 * n5 * 128 * 4 + 16 * n5 * 4
 
 
 @pytest.mark.parametrize("kw,code", [
