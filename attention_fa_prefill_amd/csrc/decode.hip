@@ -9,7 +9,8 @@
 // the splits here are combined by log-sum-exp.
 //
 // Split kernel: one work-group (4 waves) per (sequence b, kv head g, group of
-// up to 16 query heads sharing g, split s of tps tokens). Waves take 32-token
+// up to 16 query heads sharing g, split s of tps tokens), live splits numbered
+// densely so that the XCDs get equal shares of a mixed-length batch. Waves take 32-token
 // steps round-robin and keep two steps of loads in flight. Per step:
 //   - K rows go HBM -> VGPRs directly in the A-operand layout of
 //     v_mfma_f32_16x16x32_bf16 (16 tokens x 32 dims per MFMA);
@@ -85,9 +86,64 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int s = blockIdx.x;
-  const int g = blockIdx.y / p.hchunks, hc = blockIdx.y % p.hchunks;
-  const int b = blockIdx.z;
+  // blockIdx.x = gh * (B * nsplit) + item: one block of work-groups per (kv
+  // head, query-head chunk) pair gh, the splits of all sequences inside it.
+  const int per_gh = p.B * p.nsplit;
+  const int gh = blockIdx.x / per_gh;
+  const int item = blockIdx.x % per_gh;
+  auto splits_of = [&](int l) __attribute__((always_inline)) {
+    l = l < 0 ? 0 : (l > p.max_len ? p.max_len : l);
+    return (l + p.tps - 1) / p.tps;
+  };
+  int b, s;
+  if (p.compact) {
+    // Live splits are numbered densely, sequence by sequence, so consecutive
+    // work-groups (which the dispatcher deals round-robin to the 8 XCDs) carry
+    // work and every XCD gets an equal share whatever the length mix; the
+    // items past the last live split exit at once.
+    // Each thread counts the splits of a run of sequences; a block-wide scan
+    // gives the run offsets; the thread whose run holds this item finds it.
+    __shared__ int sWave[4], sItem[2];
+    const int C = (p.B + 255) / 256;
+    const int b0 = tid * C, b1 = min(p.B, b0 + C);
+    int cnt = 0;
+    for (int bb = b0; bb < b1; ++bb) cnt += splits_of(p.lens[bb]);
+    int inc = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off);
+      if (lane >= off) inc += y;
+    }
+    if (lane == 63) sWave[w] = inc;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      before += u < w ? sWave[u] : 0;
+      total += sWave[u];
+    }
+    if (item >= total) return;  // past the last live split (uniform)
+    const int excl = before + inc - cnt;
+    if (item >= excl && item < excl + cnt) {
+      int acc = excl;
+      for (int bb = b0; bb < b1; ++bb) {
+        const int n = splits_of(p.lens[bb]);
+        if (item < acc + n) {
+          sItem[0] = bb;
+          sItem[1] = item - acc;
+          break;
+        }
+        acc += n;
+      }
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(sItem[0]);
+    s = __builtin_amdgcn_readfirstlane(sItem[1]);
+  } else {
+    s = item % p.nsplit;
+    b = item / p.nsplit;
+  }
+  const int g = gh / p.hchunks, hc = gh % p.hchunks;
   int len = p.lens[b];
   len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
   const int tok0 = s * p.tps;
@@ -303,95 +359,107 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   }
 }
 
-// Merge: one work-group of 256 threads per output row. M = max of the row's
-// log-sum-exps (wave shuffles, then LDS across the 4 waves); then D/4 threads
-// per split read 16 bytes each, so one split's row is one coalesced access,
-// and 256/(D/4) split groups stride over the splits, 4 splits per round.
+// Merge: one work-group of 256 threads per (output row, 32 output dims).
+// 8 threads cover a split's 32 dims with one 16-byte load each (one 128-byte
+// access per split), 32 split groups stride over the splits, and each thread
+// loads 8 splits' log-sum-exps and partial outputs together before using them,
+// so a row of up to 256 splits is read in one round trip. Each thread keeps a
+// running max and rescales its sums when the max rises (no separate pass for
+// the max); the 32 group states are then combined in LDS the same way.
 // Splits whose lse is -inf carry no weight and their partial output is ignored.
 template <int D>
 __global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
-  constexpr int TPR = D / 4;     // threads per split row
-  constexpr int NG = 256 / TPR;  // split groups
-  __shared__ float red[4];
-  __shared__ float4 accs[NG][TPR];
-  __shared__ float wsum_s[NG];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r = blockIdx.x;
+  constexpr int CW = 32;          // output dims per work-group
+  constexpr int TPS = CW / 4;     // threads per split
+  constexpr int NG = 256 / TPS;   // split groups
+  constexpr int U = 8;            // splits per thread per round
+  __shared__ float sm[4], sw[NG];
+  __shared__ float4 sa[NG][TPS];
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x, cb = blockIdx.y;
   int nS = p.S;
   if (p.lens) {
     int len = p.lens[r / p.Hq];
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
     nS = (len + p.tps - 1) / p.tps;
   }
+  const int c = tid % TPS, sg = tid / TPS;
   const float* lse = p.lse + (size_t)r * p.S;
-  float M = -INFINITY;
-  for (int s = tid; s < nS; s += 256) M = fmaxf(M, lse[s]);
+  const float* op = p.o_parts + (size_t)r * p.S * D + CW * cb + 4 * c;
+  float m = -INFINITY, W = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < nS; s0 += NG * U) {
+    float l[U];
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u * NG + sg;
+      l[u] = -INFINITY;
+      x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (s < nS) {
+        l[u] = lse[s];
+        x[u] = *(const float4*)(op + (size_t)s * D);
+      }
+    }
+    float mr = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mr = fmaxf(mr, l[u]);
+    if (mr != -INFINITY) {
+      const float sc = (m == -INFINITY) ? 0.f : expf(m - mr);
+      W *= sc;
+      acc.x *= sc; acc.y *= sc; acc.z *= sc; acc.w *= sc;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (l[u] != -INFINITY) {
+          const float wt = expf(l[u] - mr);
+          W += wt;
+          acc.x = fmaf(wt, x[u].x, acc.x);
+          acc.y = fmaf(wt, x[u].y, acc.y);
+          acc.z = fmaf(wt, x[u].z, acc.z);
+          acc.w = fmaf(wt, x[u].w, acc.w);
+        }
+      }
+      m = mr;
+    }
+  }
+  // combine the groups: M = max of the group maxima, every thread rescales its
+  // own group's sums by exp(m - M), then plain sums over the groups
+  float M = m;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if (lane == 0) red[w] = M;
+  if ((tid & 63) == 0) sm[tid >> 6] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-
-  const int c = tid % TPR, sg = tid / TPR;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float W = 0.f;
-  if (M != -INFINITY) {
-    const float* op = p.o_parts + (size_t)r * p.S * D + 4 * c;
-    auto add = [&](float l, float4 x) __attribute__((always_inline)) {
-      const bool live = l != -INFINITY;
-      const float wt = live ? expf(l - M) : 0.f;
-      W += wt;
-      if (live) {
-        acc.x = fmaf(wt, x.x, acc.x);
-        acc.y = fmaf(wt, x.y, acc.y);
-        acc.z = fmaf(wt, x.z, acc.z);
-        acc.w = fmaf(wt, x.w, acc.w);
-      }
-    };
-    int s = sg;
-    for (; s + 3 * NG < nS; s += 4 * NG) {
-      float l[4];
-      float4 x[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        l[u] = lse[s + u * NG];
-        x[u] = *(const float4*)(op + (size_t)(s + u * NG) * D);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) add(l[u], x[u]);
-    }
-    for (; s < nS; s += NG) add(lse[s], *(const float4*)(op + (size_t)s * D));
-  }
-  accs[sg][c] = acc;
-  if (c == 0) wsum_s[sg] = W;
+  M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  const float f = (m == -INFINITY) ? 0.f : expf(m - M);
+  acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+  sa[sg][c] = acc;
+  if (c == 0) sw[sg] = W * f;
   __syncthreads();
-  if (tid < TPR) {
+  if (tid < TPS) {
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     float wsum = 0.f;
-#pragma unroll
-    for (int u = 0; u < NG; ++u) {
-      const float4 x = accs[u][tid];
-      a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
-      wsum += wsum_s[u];
+#pragma unroll 8
+    for (int g = 0; g < NG; ++g) {
+      const float4 xg = sa[g][tid];
+      a.x += xg.x; a.y += xg.y; a.z += xg.z; a.w += xg.w;
+      wsum += sw[g];
     }
     const bool empty = M == -INFINITY;
     const float inv = empty ? 0.f : 1.0f / wsum;
     const float v0 = a.x * inv, v1 = a.y * inv, v2 = a.z * inv, v3 = a.w * inv;
-    if (p.out_bf16) {
-      __bf16* dst = (__bf16*)p.o + (size_t)r * D + 4 * tid;
-      const uint2 pk = make_uint2(pack2(v0, v1), pack2(v2, v3));
-      *(uint2*)dst = pk;
-    } else {
-      *(float4*)((float*)p.o + (size_t)r * D + 4 * tid) = make_float4(v0, v1, v2, v3);
-    }
-    if (p.lse_out && tid == 0) p.lse_out[r] = empty ? -INFINITY : M + logf(wsum);
+    const size_t o_off = (size_t)r * D + CW * cb + 4 * tid;
+    if (p.out_bf16)
+      *(uint2*)((__bf16*)p.o + o_off) = make_uint2(pack2(v0, v1), pack2(v2, v3));
+    else
+      *(float4*)((float*)p.o + o_off) = make_float4(v0, v1, v2, v3);
+    if (p.lse_out && cb == 0 && tid == 0) p.lse_out[r] = empty ? -INFINITY : M + logf(wsum);
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) {
-  dim3 grid(p.nsplit, p.Hkv * p.hchunks, p.B), block(256);
+  dim3 grid(p.B * p.nsplit * p.Hkv * p.hchunks), block(256);
   if (d == 128)
     hipLaunchKernelGGL(decode_split_kernel<128>, grid, block, 0, stream, p);
   else
@@ -414,7 +482,7 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) 
 }
 
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream) {
-  dim3 grid(p.R), block(256);
+  dim3 grid(p.R, d / 32), block(256);
   if (d == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, p);
   else

@@ -13,6 +13,7 @@ constexpr int kMinDefaultTps = 64;
 constexpr int kMaxDefaultTps = 1024;
 constexpr int kTargetSplitGroups = 512;  // two resident split work-groups per CU
 constexpr int kMaxTps = 2048;
+constexpr int kCompactMaxB = 4096;  // up to 16 sequences scanned per thread of a split work-group
 constexpr int kMaxGridYZ = 65535;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -135,7 +136,8 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
   const int G = Hq / Hkv;
   const int hchunks = (G + 15) / 16;
-  if (B > kMaxGridYZ || (long)Hkv * hchunks > kMaxGridYZ) return FA_ERR_SHAPE;
+  const long nsplit_l = ((long)max_kv_len + tps - 1) / tps;
+  if ((long)B * nsplit_l * Hkv * hchunks > (long)INT32_MAX) return FA_ERR_SHAPE;
   if (!block_table && (size_t)B * (size_t)max_kv_len > (size_t)INT32_MAX) return FA_ERR_SHAPE;
   const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_kv_len, tps);
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
@@ -149,6 +151,7 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   p.nsplit = (max_kv_len + tps - 1) / tps;
   p.G = G;
   p.hchunks = hchunks;
+  p.compact = B <= kCompactMaxB ? 1 : 0;
   // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0
   p.c = fmaxf(fabsf(scale) * fa::kLog2e, 1e-30f);
   p.neg = scale < 0.f ? 1 : 0;

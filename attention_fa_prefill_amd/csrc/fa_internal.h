@@ -50,6 +50,7 @@ struct DecodeParams {
   int hchunks;         // ceil(G / 16)
   float c;             // |scale| * log2(e)
   int neg;
+  int compact;         // number live splits densely (B small enough to scan per work-group)
 };
 
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);

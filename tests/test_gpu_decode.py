@@ -118,6 +118,20 @@ def test_head_groups_and_split_sizes(G, Hkv, d, tps):
     assert_bf16_close(host_f64(o), oracle_out(case), f"{case.name} G={G} tps={tps}")
 
 
+@pytest.mark.parametrize("B", [300, 4096, 4100])
+def test_many_short_sequences(B):
+    """Large batches of short mixed-length sequences (zeros included). Up to
+    4096 sequences the live splits are numbered densely by a scan over all
+    lengths in every work-group (16 sequences per thread at 4096); above that
+    the plain numbering is used. Either way every split must be covered once."""
+    lens = np.random.default_rng(B).integers(0, 97, size=B).astype(np.int32)
+    case = workloads.decode_contiguous(B, 2, 1, 64, 96, seqlens=lens, seed=31, poison=True)
+    o = run(case, 32)
+    got = host_f64(o)
+    assert np.all(got[lens == 0] == 0.0)
+    assert_bf16_close(got, oracle_out(case), f"B={B}")
+
+
 def test_seqlens_clamped_to_capacity():
     lens = np.array([5000, -3], np.int32)  # above capacity and negative
     case = workloads.decode_contiguous(2, 4, 2, 128, 96, seqlens=lens, seed=23)
@@ -166,6 +180,23 @@ def test_merge_lse_against_oracle():
     assert np.max(np.abs(host_f64(lse_out)[ok] - ref_l[ok])) < 2e-5
     ob, _ = fa.merge_lse(dev_f32(op), dev_f32(ls))
     assert_bf16_close(host_f64(ob)[ok], ref_o[ok], "merge bf16")
+
+
+def test_merge_lse_many_splits():
+    """More splits than one round of the merge covers, with the maximum rising
+    across rounds (so partial sums are rescaled) and scattered empty splits."""
+    torch = torch_gpu()
+    rng = np.random.default_rng(29)
+    R, S, d = 5, 600, 64
+    op = rng.standard_normal((R, S, d)).astype(np.float32)
+    ls = (np.linspace(-40.0, 40.0, S)[None, :] + rng.standard_normal((R, S)) * 3).astype(np.float32)
+    ls[1] = ls[1][::-1]  # maximum first
+    ls[2, ::7] = -np.inf
+    op[2, ::7] = np.nan
+    o, lse_out = fa.merge_lse(dev_f32(op), dev_f32(ls), out_dtype=torch.float32)
+    ref_o, ref_l = oracle.merge(op.astype(np.float64), ls.astype(np.float64))
+    assert np.max(np.abs(host_f64(o) - ref_o)) < 2e-5
+    assert np.max(np.abs(host_f64(lse_out) - ref_l)) < 2e-5
 
 
 def test_merge_rejects_page_sum():
