@@ -1,0 +1,78 @@
+// ceiling.hip - two measurement kernels that give the practical ceilings the
+// attention kernels are compared with on the same GPU (not part of the
+// attention path, and linked into a library of their own):
+//   - a plain streaming read: every work-group reads one contiguous chunk of a
+//     buffer with 16-byte loads, 8 in flight per thread, and folds the words
+//     into a value that is stored only if it matches an impossible pattern;
+//   - an MFMA loop: each wave runs 8 independent accumulator chains of
+//     v_mfma_f32_32x32x16_bf16 (32768 FLOP each) for a given number of rounds.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(256) read_kernel(const uint4* __restrict__ p, long n16, unsigned* sink) {
+  constexpr int U = 8;
+  const long chunk = (n16 + gridDim.x - 1) / gridDim.x;
+  const long b0 = (long)blockIdx.x * chunk;
+  const long b1 = b0 + chunk < n16 ? b0 + chunk : n16;
+  unsigned acc = 0;
+  long i = b0 + threadIdx.x;
+  for (; i + (U - 1) * 256 < b1; i += U * 256) {
+    uint4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) x[u] = p[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= x[u].x ^ x[u].y ^ x[u].z ^ x[u].w;
+  }
+  for (; i < b1; i += 256) {
+    const uint4 x = p[i];
+    acc ^= x.x ^ x.y ^ x.z ^ x.w;
+  }
+  if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
+}
+
+__global__ void __launch_bounds__(256) mfma_kernel(unsigned* sink, int rounds) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(float)(threadIdx.x + i);
+    b[i] = (__bf16)(float)(i - (int)threadIdx.x);
+  }
+  f32x16 c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = f32x16{};
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][15];
+  if (s == 1234.5f) sink[blockIdx.x] = 1u;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads `bytes` (a multiple of 16, 16-byte aligned) from device buffer p with
+// `grid` work-groups of 256 threads; sink must hold `grid` words (never
+// written in practice). Returns the hipError_t of the launch.
+int fa_ceiling_read(const void* p, long bytes, void* sink, int grid, void* stream) {
+  hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const uint4*)p, bytes / 16,
+                     (unsigned*)sink);
+  return (int)hipGetLastError();
+}
+
+// Runs grid x 4 waves of the MFMA loop: 8 * rounds MFMAs of 32768 FLOP each
+// per wave. sink must hold `grid` words. Returns the hipError_t of the launch.
+int fa_ceiling_mfma(void* sink, int grid, int rounds, void* stream) {
+  hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (unsigned*)sink, rounds);
+  return (int)hipGetLastError();
+}
+
+}  // extern "C"

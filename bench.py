@@ -13,11 +13,15 @@ Also reported on the same JSON line:
     on the current kernel source, else null;
   - decode: contiguous 32k (B=4), paged mixed lengths (B=8) and long-context
     256k (B=1): us/call (both kernels) and algorithmic HBM GB/s against 8 TB/s,
-    each call timed alone after a 1 GiB write that evicts the 256 MB
-    last-level cache;
+    each call timed alone after a 1 GiB read that evicts the 256 MB
+    last-level cache (a read leaves no dirty lines behind);
   - us/call at B=1 for the fp32 single-head prefill and the bf16 prefill;
-  - cpu_baseline: the fp64 oracle on the full prefill workload, host cores.
+  - ceilings: a plain streaming-read kernel's GB/s and an MFMA-loop kernel's
+    bf16 TFLOP/s on the same GPU, the practical limits next to the peaks;
+  - cpu_baseline: the fp64 oracle on the full prefill workload, host cores,
+    repeated for about 10 s.
 Only one GPU is used; --gpus above 1 exits with a message.
+--prefill-only and --decode-only run one leg (for profiler passes).
 """
 from __future__ import annotations
 
@@ -93,6 +97,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode and latency legs")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the decode leg and print its results (not the headline line)")
     ap.add_argument("--decode-reps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device-to-device copies (HBM counter calibration)")
@@ -129,83 +135,36 @@ def main():
     def i32(x):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(dev)
 
-    # ------------------------------------------------------------------ headline: GQA causal prefill
-    case = workloads.prefill_gqa_2k()
-    q, k, v = bf16(case.q), bf16(case.k), bf16(case.v)
-    o = torch.empty_like(q)
-    L = fa.lib()
-    B, Hq, Hkv, Sq, Skv, d = case.B, case.Hq, case.Hkv, case.Sq, case.Skv, case.d
-    hstream = ctypes_stream = None
     import ctypes
 
+    L = fa.lib()
     ctypes_stream = ctypes.c_void_p(stream.cuda_stream)
-    argv = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-            ctypes.c_void_p(o.data_ptr()), B, Hq, Hkv, Sq, Skv, d, case.scale, 1, ctypes_stream)
 
-    def step():
-        st = L.fa_prefill(*argv)
-        if st != 0:
-            raise RuntimeError(fa.status_string(st))
+    # Eviction buffer: 1 GiB, four times the 256 MB last-level (Infinity)
+    # cache. It is READ before each cold call: a write here would leave
+    # dirty lines whose write-back would then compete with the timed
+    # kernel's reads and understate its bandwidth.
+    flush = None
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        step()
-        ev[i][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = total_ms / K
-    flops = prefill_flops(B, Hq, Sq, Skv, d, True)
-    value = flops / (ms_per_step * 1e-3) / 1e12
-    mean_launch_ms = statistics.fmean(launch_ms)
-    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
-    traffic = traffic_for("prefill_bf16_kernel<128>@prefill_gqa_b1h32x8s2048d128", PREFILL_KERNEL_SRC)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "prefill_bf16_kernel<128>", "mean_launch_us": round(mean_launch_ms * 1e3, 2),
-                "algorithmic_flop_per_launch": flops,
-                "algorithmic_bytes_per_launch": prefill_bytes(B, Hq, Hkv, Sq, Skv, d)}
+    def timed_calls(fn, reps, evict):
+        nonlocal flush
+        if evict and flush is None:
+            flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        times = []
+        for _ in range(3):
+            fn()
+        for _ in range(reps):
+            if evict:
+                torch.amax(flush)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        return times
 
-    result = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-              "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
-              "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-              "config": {"workload": case.name, "B": B, "Hq": Hq, "Hkv": Hkv, "Sq": Sq, "Skv": Skv, "d": d,
-                         "causal": True, "scale": case.scale, "seed": 1002},
-              "roofline": roofline,
-              "prefill_us_per_call_p50": round(statistics.median(launch_ms) * 1e3, 2)}
-
-    # ------------------------------------------------------------------ decode and latency legs
-    if not args.prefill_only:
-        # Eviction buffer: 1 GiB, four times the 256 MB last-level (Infinity)
-        # cache. It is READ before each cold call: a write here would leave
-        # dirty lines whose write-back would then compete with the timed
-        # kernel's reads and understate its bandwidth.
-        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-
-        def timed_calls(fn, reps, evict):
-            times = []
-            for _ in range(3):
-                fn()
-            for _ in range(reps):
-                if evict:
-                    torch.amax(flush)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                fn()
-                b.record(stream)
-                b.synchronize()
-                times.append(a.elapsed_time(b) * 1e3)
-            return times
-
+    def decode_leg():
         dec = {}
         for dc in (workloads.decode_contig_32k(), workloads.decode_paged_mixed(), workloads.decode_long_256k()):
             dq, dk, dv = bf16(dc.q), bf16(dc.kcache), bf16(dc.vcache)
@@ -240,6 +199,71 @@ def main():
                             "splits_per_sequence": -(-dc.max_kv_len // tps)}
             del dq, dk, dv, ws, od, lens, bt
             torch.cuda.empty_cache()
+        return dec
+
+    if args.decode_only:
+        print(json.dumps({"decode": decode_leg()}), flush=True)
+        return
+
+    # ------------------------------------------------------------------ headline: GQA causal prefill
+    case = workloads.prefill_gqa_2k()
+    q, k, v = bf16(case.q), bf16(case.k), bf16(case.v)
+    o = torch.empty_like(q)
+    B, Hq, Hkv, Sq, Skv, d = case.B, case.Hq, case.Hkv, case.Sq, case.Skv, case.d
+    argv = (ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(o.data_ptr()), B, Hq, Hkv, Sq, Skv, d, case.scale, 1, ctypes_stream)
+
+    def step():
+        st = L.fa_prefill(*argv)
+        if st != 0:
+            raise RuntimeError(fa.status_string(st))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    # Timed region: K back-to-back calls between one pair of events on the
+    # launch stream (no events in between, which would add their own gaps).
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(K):
+        step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+    flops = prefill_flops(B, Hq, Sq, Skv, d, True)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    mean_launch_ms = ms_per_step  # one kernel per call: the mean launch duration over the timed region
+    achieved = flops / (mean_launch_ms * 1e-3) / 1e12
+    # separately: isolated calls, each between its own pair of events (latency per call)
+    launch_ms = []
+    for _ in range(min(K, 50)):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        b.synchronize()
+        launch_ms.append(a.elapsed_time(b))
+    traffic = traffic_for("prefill_bf16_kernel<128>@prefill_gqa_b1h32x8s2048d128", PREFILL_KERNEL_SRC)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "prefill_bf16_kernel<128>", "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                "algorithmic_flop_per_launch": flops,
+                "algorithmic_bytes_per_launch": prefill_bytes(B, Hq, Hkv, Sq, Skv, d)}
+
+    result = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
+              "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+              "config": {"workload": case.name, "B": B, "Hq": Hq, "Hkv": Hkv, "Sq": Sq, "Skv": Skv, "d": d,
+                         "causal": True, "scale": case.scale, "seed": 1002},
+              "roofline": roofline,
+              "prefill_us_per_call_p50": round(statistics.median(launch_ms) * 1e3, 2)}
+
+    # ------------------------------------------------------------------ decode and latency legs
+    if not args.prefill_only:
+        dec = decode_leg()
         result["decode"] = dec
         traffic_dec = traffic_for("decode_split_kernel<128>@decode_long_b1h16x2kv256kd128", DECODE_KERNEL_SRC)
         long = dec["decode_long_b1h16x2kv256kd128"]
@@ -274,17 +298,54 @@ def main():
             "decode_long_b1h16x2kv256kd128": {"us_per_call_p50": long["us_per_call_p50"]},
         }
 
+        # ------------------------------------------------------------------ practical ceilings
+        C = ctypes.CDLL(os.path.join(ROOT, "attention_fa_prefill_amd", "libfa_ceiling.so"))
+        C.fa_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+        C.fa_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        rbuf = torch.ones(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
+        rbytes = rbuf.numel() * 4
+        sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
+
+        def read_call():
+            if C.fa_ceiling_read(ctypes.c_void_p(rbuf.data_ptr()), rbytes, ctypes.c_void_p(sink.data_ptr()), 2048,
+                                 ctypes_stream) != 0:
+                raise RuntimeError("ceiling read kernel launch failed")
+
+        mm_grid, mm_rounds = 512, 1000
+        mm_flop = mm_grid * 4 * 8 * mm_rounds * 32768
+
+        def mfma_call():
+            if C.fa_ceiling_mfma(ctypes.c_void_p(sink.data_ptr()), mm_grid, mm_rounds, ctypes_stream) != 0:
+                raise RuntimeError("ceiling mfma kernel launch failed")
+
+        t_rd = statistics.median(timed_calls(read_call, 20, evict=True))
+        t_mm = statistics.median(timed_calls(mfma_call, 10, evict=False))
+        del rbuf
+        torch.cuda.empty_cache()
+        result["ceilings"] = {
+            "stream_read_GB_per_s": round(rbytes / (t_rd * 1e-6) / 1e9, 1),
+            "stream_read_frac_of_hbm_peak": round(rbytes / (t_rd * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "mfma_loop_bf16_TFLOP_per_s": round(mm_flop / (t_mm * 1e-6) / 1e12, 1),
+            "mfma_loop_frac_of_bf16_peak": round(mm_flop / (t_mm * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "plain 512 MiB streaming read (caches evicted) and an 8-chain v_mfma_f32_32x32x16_bf16 loop, "
+                    "timed per call with HIP events like the attention calls"}
+
     # ------------------------------------------------------------------ CPU baseline: the oracle
     if not args.no_cpu_baseline:
         import oracle
 
         qf, kf, vf = case.as_f64()
-        t0 = time.perf_counter()
-        oracle.attention(qf, kf, vf, case.scale, True)
-        dt = time.perf_counter() - t0
+        runs = []
+        t_all = time.perf_counter()
+        while not runs or time.perf_counter() - t_all < 10.0:
+            t0 = time.perf_counter()
+            oracle.attention(qf, kf, vf, case.scale, True)
+            runs.append(time.perf_counter() - t0)
+        dt = statistics.median(runs)
         result["cpu_baseline"] = {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s",
                                   "cores": oracle.num_threads(), "kind": "oracle",
-                                  "sample": f"the whole {case.name} workload once (fp64, {dt:.2f} s wall)"}
+                                  "sample": f"the whole {case.name} workload (fp64), {len(runs)} runs in "
+                                            f"{sum(runs):.1f} s, median {dt:.3f} s per run"}
     print(json.dumps(result), flush=True)
 
 
