@@ -47,6 +47,7 @@ namespace {
 constexpr int kBM = 128;     // query rows per wave group
 constexpr int kBN = 64;      // keys per KV block
 constexpr float kTau = 8.0f; // lazy rescale threshold (log2 units)
+constexpr float kRedo = 65536.0f;  // partial row sum above which a block is redone with its maximum
 constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
@@ -173,6 +174,15 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   }
   // One K or V block -> this group's slot of an LDS stage. The buffer resource
   // covers only the keys that exist, so rows past Skv read as zero.
+  auto dma_one = [&](const __bf16* src_bh, __bf16* stage, const uint32_t* offs, int j, bool valid, int ii) __attribute__((always_inline)) {
+    const int kv0 = j * kBN;
+    const int rows = valid ? min(kBN, Skv - kv0) : 0;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src_bh + (size_t)(valid ? kv0 : 0) * D), (short)0, rows * D * 2, kRsrcWord3);
+    __bf16* dst0 = stage + grp * C::ELEMS;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst0 + 64 * (wg * C::NI + ii) * 8), 16, (int)offs[ii], 0,
+                                             0, 0);
+  };
   auto dma = [&](const __bf16* src_bh, __bf16* stage, const uint32_t* offs, int j) __attribute__((always_inline)) {
     const int kv0 = j * kBN;
     const int rows = min(kBN, Skv - kv0);
@@ -316,12 +326,13 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     for (int i = 0; i < kPV + kS; ++i) {
       const bf16x8 a = buf[i % kPF];
       if (i + kPF < kPV + kS) buf[i % kPF] = opnd(i + kPF);
-      if (i + kPF == kPV) {
-        // all V reads of this slot are issued: start the loads for later slots
-        __builtin_amdgcn_sched_barrier(0);
-        if (k + 1 < cnt) dma(kbh, sKn, koff, kv_of(k + 1));
-        if (k < cnt) dma(vbh, sVc, voff, kv_of(k));
-        __builtin_amdgcn_sched_barrier(0);
+      if (i >= kPV && i < kPV + 4 * C::NI && ((i - kPV) & 1) == 0) {
+        // one direct-to-LDS load between MFMAs: K of block k+1, then V of block k
+        const int n = (i - kPV) >> 1;
+        if (n < C::NI)
+          dma_one(kbh, sKn, koff, kv_of(k + 1), k + 1 < cnt, n);
+        else
+          dma_one(vbh, sVc, voff, kv_of(k), k < cnt, n - C::NI);
       }
       if (i < kPV) {
         const int sub = i / (2 * C::DB), ss = (i / C::DB) & 1, db = i % C::DB;
@@ -345,9 +356,6 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
       // group A moving from t0 to t1 (Q of t1 staged in LDS): the scores above
       // used t0's Q; finish t0, then redo S with t1's Q.
       store_tile(cur_tile);
-      // Let the stores drain here, once, so that no store is still reading its
-      // data registers when the loop reuses them.
-      wait_dma();
       reset_state();
       load_q_lds();
       cur_tile = t;
@@ -367,16 +375,18 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   };
 
   // Vector slot: softmax of the block in S0/S1 -> P, with the online update.
+  // The exponent reference m_run only has to keep the probabilities in range,
+  // not to be the exact row maximum (any reference gives the same normalised
+  // result). So a block is first exponentiated against the current reference
+  // without looking for its maximum; only when a row has no reference yet, or
+  // when a row's partial sum shows that the block rose far above it
+  // (> 2^16), is the block's maximum taken, the reference raised (lazily, by
+  // more than kTau) with O and l rescaled, and the block redone.
   auto vslot = [&]() __attribute__((always_inline)) {
     if (!s_vis) return;
     const int kv0 = s_kv0, q0 = s_q0;
     const bool full = kv0 + kBN <= Skv && (!causal || kv0 + kBN - 1 <= q0 + off);
-    float mx;
-    if (full) {
-      mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-    } else {
+    if (!full) {
       // key of register r of sub-tile u is kb + 8*(r/4) + (r%4), kb = kv0 + 32u + 4hl;
       // visible iff < Skv and (non-causal or) <= query row + off
       const int kb = kv0 + 4 * hl;
@@ -388,41 +398,56 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
         if (ko > lim) S0[r] = -INFINITY;
         if (ko + 32 > lim) S1[r] = -INFINITY;
       }
-      mx = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
     }
-    mx = pair_max(mx);
-    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
     float alpha = 1.f;
-    if (cand > m_run + kTau) {
-      alpha = fast_exp2(m_run - cand);
-      m_run = cand;
-    }
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-    // Masked scores are -inf: with c > 0 and mu finite their exp2 is exactly 0.
-    // The row sum adds the bf16-rounded probabilities two at a time with
-    // v_dot2_f32_bf16 against (1, 1): the same values the PV product uses.
-    const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
-    float la = 0.f, lb = 0.f;
+    auto raise_to_max = [&]() __attribute__((always_inline)) {
+      float mx = fmaxf(S0[0], S1[0]);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      float e[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(sub ? S1[r] : S0[r], c, -mu));
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        uint4 w;
-        w.x = pack_bf16x2(e[8 * s + 0], e[8 * s + 1]);
-        w.y = pack_bf16x2(e[8 * s + 2], e[8 * s + 3]);
-        w.z = pack_bf16x2(e[8 * s + 4], e[8 * s + 5]);
-        w.w = pack_bf16x2(e[8 * s + 6], e[8 * s + 7]);
-        P[sub][s] = __builtin_bit_cast(bf16x8, w);
-        la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.x), ones, la, false);
-        lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.y), ones, lb, false);
-        la = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.z), ones, la, false);
-        lb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w.w), ones, lb, false);
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+      mx = pair_max(mx);
+      const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+      if (cand > m_run + kTau) {
+        alpha *= fast_exp2(m_run - cand);
+        m_run = cand;
       }
+    };
+    float la, lb;
+    // Masked scores are -inf: with c > 0 and mu finite their exp2 is exactly 0.
+    // The row sum adds the fp32 probabilities with plain adds (a dot-product
+    // instruction would wait for the matrix core, which the other wave on the
+    // SIMD keeps busy); PV uses the same values rounded to bf16.
+    auto exponentiate = [&]() __attribute__((always_inline)) {
+      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+      la = 0.f;
+      lb = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(fmaf(sub ? S1[r] : S0[r], c, -mu));
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          uint4 w;
+          w.x = pack_bf16x2(e[8 * s + 0], e[8 * s + 1]);
+          w.y = pack_bf16x2(e[8 * s + 2], e[8 * s + 3]);
+          w.z = pack_bf16x2(e[8 * s + 4], e[8 * s + 5]);
+          w.w = pack_bf16x2(e[8 * s + 6], e[8 * s + 7]);
+          P[sub][s] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+          for (int r = 0; r < 8; r += 2) {
+            la += e[8 * s + r];
+            lb += e[8 * s + r + 1];
+          }
+        }
+      }
+    };
+    const bool exact = __any(m_run == -INFINITY);
+    if (exact) raise_to_max();
+    exponentiate();
+    // !(x <= bound) also catches an infinite or NaN sum
+    if (!exact && __any(!(la + lb <= kRedo))) {
+      raise_to_max();
+      exponentiate();
     }
     l_run = alpha * l_run + (la + lb);
     if (__any(alpha != 1.f)) {
@@ -460,15 +485,22 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     lds_barrier();
     ++nbar;
   }
+  // The wave in its MFMA slot gets the higher issue priority, so that its
+  // MFMAs and LDS reads go out as soon as they are ready and the softmax wave
+  // on the same SIMD fills the remaining issue cycles.
   for (int k = 0; k <= cnt; k += 2) {
     wait_dma();
     lds_barrier();
+    __builtin_amdgcn_s_setprio(1);
     mslot(k, sK0, sV1, sK1, sV0);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
     if (k < cnt) vslot();
     wait_dma();
     lds_barrier();
+    __builtin_amdgcn_s_setprio(1);
     if (k + 1 <= cnt) mslot(k + 1, sK1, sV0, sK0, sV1);
+    __builtin_amdgcn_s_setprio(0);
     lds_barrier();
     if (k + 1 < cnt) vslot();
     nbar += 4;

@@ -5,7 +5,9 @@
 
 Headline (``value``): causal GQA prefill, B=1, Hq=32, Hkv=8, Sq=Skv=2048,
 d=128, bf16 -- algorithmic TFLOP/s over exactly K back-to-back calls of
-fa_prefill (inputs resident in HBM, bracketed by device synchronisation).
+fa_prefill (inputs resident in HBM, bracketed by device synchronisation),
+after --settle-s seconds of untimed calls (the GPU clocks ramp up over about
+half a second of load) and W untimed warmup calls.
 Also reported on the same JSON line:
   - roofline of the prefill kernel: algorithmic FLOP per launch / mean launch
     duration (HIP events on the launch stream) against the bf16 dense MFMA peak;
@@ -95,6 +97,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="untimed prefill calls for at least this long before the warmup steps, so that the "
+                         "GPU clocks have left their idle state (they ramp up over ~0.5 s of load)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="skip the decode and latency legs")
     ap.add_argument("--decode-only", action="store_true",
@@ -218,6 +223,13 @@ def main():
         if st != 0:
             raise RuntimeError(fa.status_string(st))
 
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+        n_settle += 50
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -254,7 +266,8 @@ def main():
                 "algorithmic_bytes_per_launch": prefill_bytes(B, Hq, Hkv, Sq, Skv, d)}
 
     result = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": K,
-              "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+              "warmup": args.warmup, "settle_calls": n_settle, "ms_per_step": round(ms_per_step, 5),
+              "higher_is_better": True,
               "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
               "config": {"workload": case.name, "B": B, "Hq": Hq, "Hkv": Hkv, "Sq": Sq, "Skv": Skv, "d": d,
                          "causal": True, "scale": case.scale, "seed": 1002},

@@ -92,6 +92,35 @@ def test_bf16_scale_sign_and_zero(scale):
     assert_bf16_close(host_f64(o), oracle_out(case), f"{case.name} scale={scale}")
 
 
+def _ramped_case(profile, causal, seed):
+    """Keys whose magnitude follows a profile along the sequence, so that the
+    row maxima jump between key blocks (rising, falling, or one spike late),
+    far beyond the range the kernel's exponent reference tolerates without
+    being raised."""
+    import dataclasses
+
+    base = workloads.prefill_case(1, 2, 1, 700, 700, 128, causal, "bf16", seed=seed, scale=0.25)
+    k = workloads.bf16_bits_to_f32(base.k).astype(np.float64)
+    j = np.arange(700, dtype=np.float64)
+    if profile == "rising":
+        k *= (0.2 + 6.0 * j / 699.0)[None, None, :, None]
+    elif profile == "falling":
+        k *= (6.2 - 6.0 * j / 699.0)[None, None, :, None]
+    else:  # spike: one late key aligned with every query row's sum direction
+        q = workloads.bf16_bits_to_f32(base.q).astype(np.float64)
+        k[0, 0, 650, :] = 4.0 * np.sign(q[0, 0].sum(axis=0))
+    kb = workloads.f32_to_bf16_bits(k.astype(np.float32))
+    return dataclasses.replace(base, k=kb, name=f"{base.name}_{profile}")
+
+
+@pytest.mark.parametrize("profile", ["rising", "falling", "spike"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_score_jumps_between_blocks(profile, causal):
+    case = _ramped_case(profile, causal, seed=77)
+    o, _ = run_case(case)
+    assert_bf16_close(host_f64(o), oracle_out(case), case.name)
+
+
 def test_bf16_exact_cases():
     """Causal row 0 sees one key (probability exactly 1): o = V[0] bit for bit.
     With Skv = 1 every row gives v_0 exactly."""
