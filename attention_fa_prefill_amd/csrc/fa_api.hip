@@ -104,7 +104,7 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o, i
   fa_status st = check_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, scale, causal);
   if (st != FA_OK) return st;
   fa::PrefillParams p = make_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, scale, causal);
-  return from_hip(fa::launch_prefill_f32(p, d, scale, (hipStream_t)stream));
+  return from_hip(fa::launch_prefill_f32(p, d, (hipStream_t)stream));
 }
 
 int fa_decode_split_tokens(int B, int Hq, int Hkv, int max_kv_len, int tokens_per_split) {

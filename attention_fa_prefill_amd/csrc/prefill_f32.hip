@@ -3,130 +3,158 @@
 //
 // It follows the tiled recurrence of the "Real-time inference optimisation"
 // page (section "Flash Attention optimisation"): per row a running max, a
-// running sum and a rescaled accumulator over K/V tiles held on chip. The fp32
-// path serves small, launch-latency-bound shapes, so it uses the vector ALU
-// (CDNA4 has no fp32 MFMA rate worth trading accuracy for) and accurate expf.
+// running sum and a rescaled accumulator over blocks of keys, combined at the
+// end across the key splits by their log-sum-exp. The fp32 path serves small,
+// launch-latency-bound shapes (one head of 128 rows is 2 MFLOP), so it is
+// built for a short critical path rather than for throughput:
 //
-// Work-group: 256 threads own 64 query rows, 4 threads per row; each thread
-// holds D/4 consecutive dims of its row's q and of its output accumulator.
-// A dot product is a per-thread partial sum plus a 2-step reduction across the
-// 4 threads of the row (DPP quad permutes). K/V tiles of 32 rows sit in LDS and
-// every thread reads them as broadcast float4s.
+//   - a work-group (4 waves) owns 4 query rows; each wave takes every 4th block
+//     of 8 keys, so the keys of a row are split four ways;
+//   - inside a wave, 16 lanes share a row, each holding d/16 consecutive dims
+//     of q and of its accumulator; a score is a 4-FMA (or 8-FMA) partial dot
+//     product and a 16-lane sum over DPP (quad permutes, then half-row and
+//     row mirrors);
+//   - K and V rows are read straight from global memory as float4s (the four
+//     rows of a wave read the same addresses, which the cache merges), so no
+//     LDS staging and no barrier sits on the path;
+//   - probabilities use exp2 of scores pre-multiplied by scale*log2(e);
+//   - the four waves' (max, sum, accumulator) states are merged through LDS.
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
-constexpr int kRows = 64;  // query rows per work-group
-constexpr int kKT = 32;    // keys per LDS tile
+constexpr int kRowsPerWG = 4;  // query rows per work-group (one per 16 lanes)
+constexpr int kSplit = 4;      // waves = key splits
+constexpr int kKB = 8;         // keys per block
 
-__device__ __forceinline__ float quad_sum(float x) {
-  // quad_perm [1,0,3,2] then [2,3,0,1]: every lane of the quad ends with the sum.
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));   // quad [1,0,3,2]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));   // quad [2,3,0,1]
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));  // row_mirror
   return x;
 }
 
 template <int D>
-__global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillParams p, float scale) {
-  constexpr int DP = D / 4;  // dims per thread
-  __shared__ __attribute__((aligned(16))) float sK[kKT * D];
-  __shared__ __attribute__((aligned(16))) float sV[kKT * D];
+__global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillParams p) {
+  constexpr int DP = D / 16;  // dims per lane
+  __shared__ __attribute__((aligned(16))) float sAcc[kSplit][kRowsPerWG][D];
+  __shared__ float sM[kSplit][kRowsPerWG], sL[kSplit][kRowsPerWG];
 
-  const int tid = threadIdx.x;
-  const int rl = tid >> 2, part = tid & 3;
-  const int qt = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rr = lane >> 4, t = lane & 15;
+  const int r0 = blockIdx.x * kRowsPerWG;
+  const int h = blockIdx.y, b = blockIdx.z;
   const int g = (int)((long)h * p.Hkv / p.Hq);
   const int Sq = p.Sq, Skv = p.Skv, off = Skv - Sq;
   const bool causal = p.causal != 0;
-  const int row = qt * kRows + rl;
+  const int row = r0 + rr;
   const bool valid = row < Sq;
+  const float cs = p.neg ? -p.c : p.c;  // scale * log2(e)
 
   float q[DP], acc[DP];
-  const float* qrow = (const float*)p.q + (((size_t)b * p.Hq + h) * Sq + (valid ? row : 0)) * D + part * DP;
+  {
+    const float* qrow = (const float*)p.q + (((size_t)b * p.Hq + h) * Sq + (valid ? row : 0)) * D + t * DP;
 #pragma unroll
-  for (int e = 0; e < DP; e += 4) {
-    float4 x = valid ? *(const float4*)(qrow + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-    q[e] = x.x; q[e + 1] = x.y; q[e + 2] = x.z; q[e + 3] = x.w;
+    for (int e = 0; e < DP; e += 4) {
+      const float4 x = valid ? *(const float4*)(qrow + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      q[e] = x.x; q[e + 1] = x.y; q[e + 2] = x.z; q[e + 3] = x.w;
+    }
   }
 #pragma unroll
   for (int e = 0; e < DP; ++e) acc[e] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  const int last_row = min(Sq, (qt + 1) * kRows) - 1;
-  const int kend = causal ? min(Skv, last_row + off + 1) : Skv;  // keys this work-group needs
-  const int lim = causal ? row + off : Skv - 1;                    // last key visible to this row
-  const float* kbh = (const float*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
-  const float* vbh = (const float*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  // keys any row of this work-group can see; the last key this row can see
+  const int last_row = min(Sq, r0 + kRowsPerWG) - 1;
+  const int kend = causal ? min(Skv, last_row + off + 1) : Skv;
+  const int lim = causal ? min(row + off, Skv - 1) : Skv - 1;
+  const int nblk = (kend + kKB - 1) / kKB;
+  const float* kbh = (const float*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D + t * DP;
+  const float* vbh = (const float*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D + t * DP;
 
-  for (int k0 = 0; k0 < kend; k0 += kKT) {
-    __syncthreads();
-    // cooperative tile load: kKT*D floats as float4, rows past Skv clamped
-    for (int f = tid; f < kKT * D / 4; f += 256) {
-      const int r = (f * 4) / D, cidx = (f * 4) % D;
-      const int gr = min(k0 + r, Skv - 1);
-      *(float4*)(sK + r * D + cidx) = *(const float4*)(kbh + (size_t)gr * D + cidx);
-      *(float4*)(sV + r * D + cidx) = *(const float4*)(vbh + (size_t)gr * D + cidx);
-    }
-    __syncthreads();
-    float s[kKT];
-    float mx = -INFINITY;
+  for (int blk = w; blk < nblk; blk += kSplit) {
+    const int k0 = blk * kKB;
+    float kv[kKB][DP], vv[kKB][DP];
 #pragma unroll
-    for (int jj = 0; jj < kKT; ++jj) {
-      const float* kr = sK + jj * D + part * DP;
-      float sp = 0.f;
+    for (int j = 0; j < kKB; ++j) {
+      const size_t key = (size_t)min(k0 + j, Skv - 1);  // rows past Skv are masked below
 #pragma unroll
       for (int e = 0; e < DP; e += 4) {
-        const float4 x = *(const float4*)(kr + e);
-        sp = fmaf(q[e], x.x, sp);
-        sp = fmaf(q[e + 1], x.y, sp);
-        sp = fmaf(q[e + 2], x.z, sp);
-        sp = fmaf(q[e + 3], x.w, sp);
+        const float4 x = *(const float4*)(kbh + key * D + e);
+        kv[j][e] = x.x; kv[j][e + 1] = x.y; kv[j][e + 2] = x.z; kv[j][e + 3] = x.w;
+        const float4 y = *(const float4*)(vbh + key * D + e);
+        vv[j][e] = y.x; vv[j][e + 1] = y.y; vv[j][e + 2] = y.z; vv[j][e + 3] = y.w;
       }
-      sp = quad_sum(sp) * scale;
-      const int key = k0 + jj;
-      s[jj] = (key <= lim && key < Skv) ? sp : -INFINITY;
-      mx = fmaxf(mx, s[jj]);
     }
-    const float mn = fmaxf(m, mx);
-    const float alpha = (mn == -INFINITY) ? 1.f : expf(m - mn);
-    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    float s[kKB];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kKB; ++j) {
+      float sp = 0.f;
+#pragma unroll
+      for (int e = 0; e < DP; ++e) sp = fmaf(q[e], kv[j][e], sp);
+      sp = row16_sum(sp) * cs;
+      s[j] = (k0 + j <= lim) ? sp : -INFINITY;
+      bm = fmaxf(bm, s[j]);
+    }
+    const float mn = fmaxf(m, bm);
+    if (mn == -INFINITY) continue;  // nothing of this block is visible to this row yet
+    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+    m = mn;
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < DP; ++e) acc[e] *= alpha;
 #pragma unroll
-    for (int jj = 0; jj < kKT; ++jj) {
-      const float pj = (s[jj] == -INFINITY) ? 0.f : expf(s[jj] - mu);
+    for (int j = 0; j < kKB; ++j) {
+      const float pj = __builtin_amdgcn_exp2f(s[j] - mn);  // exp2(-inf) = 0 for masked keys
       l += pj;
-      const float* vr = sV + jj * D + part * DP;
 #pragma unroll
-      for (int e = 0; e < DP; e += 4) {
-        const float4 x = *(const float4*)(vr + e);
-        acc[e] = fmaf(pj, x.x, acc[e]);
-        acc[e + 1] = fmaf(pj, x.y, acc[e + 1]);
-        acc[e + 2] = fmaf(pj, x.z, acc[e + 2]);
-        acc[e + 3] = fmaf(pj, x.w, acc[e + 3]);
-      }
+      for (int e = 0; e < DP; ++e) acc[e] = fmaf(pj, vv[j][e], acc[e]);
     }
-    m = mn;
   }
-  if (valid) {
-    const float inv = 1.0f / l;
-    float* orow = (float*)p.o + (((size_t)b * p.Hq + h) * Sq + row) * D + part * DP;
+
+  // merge the four key splits: o = sum_w 2^(m_w - M) acc_w / sum_w 2^(m_w - M) l_w
 #pragma unroll
-    for (int e = 0; e < DP; e += 4)
-      *(float4*)(orow + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+  for (int e = 0; e < DP; ++e) sAcc[w][rr][t * DP + e] = acc[e];
+  if (t == 0) {
+    sM[w][rr] = m;
+    sL[w][rr] = l;
   }
+  __syncthreads();
+  if (w != 0 || !valid) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int u = 0; u < kSplit; ++u) M = fmaxf(M, sM[u][rr]);
+  float L = 0.f, o[DP];
+#pragma unroll
+  for (int e = 0; e < DP; ++e) o[e] = 0.f;
+#pragma unroll
+  for (int u = 0; u < kSplit; ++u) {
+    const float mu = sM[u][rr];
+    const float f = (mu == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mu - M);
+    L = fmaf(f, sL[u][rr], L);
+#pragma unroll
+    for (int e = 0; e < DP; ++e) o[e] = fmaf(f, sAcc[u][rr][t * DP + e], o[e]);
+  }
+  const float inv = 1.0f / L;
+  float* orow = (float*)p.o + (((size_t)b * p.Hq + h) * Sq + row) * D + t * DP;
+#pragma unroll
+  for (int e = 0; e < DP; e += 4)
+    *(float4*)(orow + e) = make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
 }
 
 }  // namespace
 
-hipError_t launch_prefill_f32(const PrefillParams& p, int d, float scale, hipStream_t stream) {
-  dim3 grid((p.Sq + kRows - 1) / kRows, p.Hq, p.B), block(256);
+hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream) {
+  dim3 grid((p.Sq + kRowsPerWG - 1) / kRowsPerWG, p.Hq, p.B), block(256);
   if (d == 128)
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, p, scale);
+    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, p, scale);
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
