@@ -59,7 +59,6 @@ struct Cfg {
   static constexpr int KS = D / 16;              // k-steps of S^T = K . Q^T
   static constexpr int DB = D / 32;              // 32-row d blocks of O^T
   static constexpr int XO = 64 * DB * 16;        // floats of one wave's O^T in the exchange
-  static constexpr int QI = 32 * CH / 64;        // direct-to-LDS loads per wave for its Q rows
 };
 
 // LDS swizzles (16-byte chunk index XOR a function of the row).
@@ -221,20 +220,19 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
       qreg[ks] = __builtin_bit_cast(bf16x8, x);
     }
   };
-  // Group A stages its second tile's Q rows in LDS at the start (each wave its
-  // own 32 rows), so the tile switch costs LDS reads instead of HBM latency.
-  auto stage_q = [&](int t) __attribute__((always_inline)) {
-    const int row0 = t * kBM + wg * 32;
-    const int rows = max(0, min(32, Sq - row0));
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(qbh + (size_t)row0 * D), (short)0, rows * D * 2, kRsrcWord3);
+  // Group A needs its second tile's Q (tile t1) at the tile switch; group B
+  // holds exactly those rows in registers (its only tile is t1), so each B
+  // wave writes them to LDS in the prologue, in the layout load_q_lds reads
+  // (the same lane owns the same 16 bytes on both sides), without the sign
+  // flip. No second read of Q from memory.
+  auto share_q = [&]() __attribute__((always_inline)) {
+    const int row = wg * 32 + ln;
+    char* base = (char*)sQ + row * (D * 2);
 #pragma unroll
-    for (int ii = 0; ii < C::QI; ++ii) {
-      const int P = 64 * ii + lane;
-      const int row = P / C::CH, pc = P % C::CH;
-      const int voffs = (row * D + ((pc ^ swz_k<D>(row)) << 3)) * 2;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(sQ + (wg * 32) * D + 64 * ii * 8), 16, voffs, 0, 0,
-                                               0);
+    for (int ks = 0; ks < C::KS; ++ks) {
+      uint4 x = __builtin_bit_cast(uint4, qreg[ks]);
+      x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
+      *(uint4*)(base + (((2 * ks + hl) ^ swz_k<D>(row)) << 4)) = x;
     }
   };
   auto load_q_lds = [&]() __attribute__((always_inline)) {
@@ -461,7 +459,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
 
   // ---- prologue: zero this group's V slot of stage 1 (the first MFMA slot
   // reads it with zero probabilities), first K block and first Q tile of each
-  // group, group A's second Q tile.
+  // group; group B shares its Q tile (group A's second) through LDS.
   {
     uint4* z = (uint4*)(sV1 + grp * C::ELEMS) + wg * (C::ELEMS / 8 / 4);
 #pragma unroll
@@ -473,7 +471,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     reset_state();
     load_q_global(cur_tile);
   }
-  if (grp == 0 && cntA > nA0 && nA0 > 0) stage_q(t1);
+  if (grp == 1 && cntA > nA0 && nA0 > 0) share_q();
 
   // ---- slots. Every wave runs the same sequence M(0) V(0) M(1) V(1) ...,
   // one barrier per slot; group B takes one empty slot first, so its MFMA slots
