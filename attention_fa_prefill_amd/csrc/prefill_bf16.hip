@@ -25,9 +25,12 @@
 //   S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T held
 //   in VGPRs), so each lane holds 16 scores of one query; the row max needs only
 //   an in-lane max and one v_permlane32_swap with the other half-wave.
-//   P = exp2(S*c - m) with c = scale*log2(e); the running max is raised lazily
-//   (only when it grows by more than kTau, in log2 units), which changes no
-//   result in exact arithmetic and skips most accumulator rescales.
+//   P = exp2(S*c - m) with c = scale*log2(e). m is an exponent reference, not
+//   necessarily the exact running max: a block is exponentiated against the
+//   current m without a max search, and the max is taken (m raised by more
+//   than kTau, O and l rescaled, block redone) only when a row has no
+//   reference yet or its block sum exceeds kRedo. Any reference gives the same
+//   normalised result in exact arithmetic.
 //   O^T += V^T . P^T on the same MFMA: A = V^T read with ds_read_b64_tr_b16
 //   from the row-major V tile in LDS, B = P^T straight from the score registers
 //   (the contraction order over keys is permuted to match their lane layout).
@@ -39,6 +42,9 @@
 // wave issues MFMA while the other issues the softmax. The barriers only order
 // LDS (no wait for outstanding HBM loads): a group waits for its own
 // direct-to-LDS loads right before the barrier that opens its next MFMA slot.
+// The loads of a block are issued one at a time between the S MFMAs of the
+// slot before (K of block k+1 and V of block k during M(k)), and the wave in
+// its MFMA slot runs at raised issue priority (s_setprio 1).
 #include "fa_internal.h"
 
 namespace fa {

@@ -32,6 +32,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import statistics
 import sys
 import time
@@ -74,8 +75,14 @@ def decode_bytes(case):
 
 
 def sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Fingerprint of a kernel source's code: comments and blank space are
+    dropped first, so that editing a comment does not void the counter data."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def traffic_for(kernel_key, src_path):
