@@ -86,21 +86,21 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // blockIdx.x = gh * (B * nsplit) + item: one block of work-groups per (kv
-  // head, query-head chunk) pair gh, the splits of all sequences inside it.
-  const int per_gh = p.B * p.nsplit;
-  const int gh = blockIdx.x / per_gh;
-  const int item = blockIdx.x % per_gh;
+  // blockIdx.x = gh * (splits per gh) + item: one block of work-groups per
+  // (kv head, query-head chunk) pair gh, the splits of all sequences inside it.
+  int gh, item;
   auto splits_of = [&](int l) __attribute__((always_inline)) {
     l = l < 0 ? 0 : (l > p.max_len ? p.max_len : l);
     return (l + p.tps - 1) / p.tps;
   };
   int b, s;
   if (p.compact) {
-    // Live splits are numbered densely, sequence by sequence, so consecutive
-    // work-groups (which the dispatcher deals round-robin to the 8 XCDs) carry
-    // work and every XCD gets an equal share whatever the length mix; the
-    // items past the last live split exit at once.
+    // Live splits are numbered densely, sequence by sequence, within each gh
+    // and the gh blocks follow each other without gaps, so the first
+    // work-groups of the grid (the ones the dispatcher starts first and deals
+    // round-robin to the 8 XCDs) all carry work, every XCD gets an equal share
+    // whatever the length mix, and the work-groups past the last live split
+    // exit at once.
     // Each thread counts the splits of a run of sequences; a block-wide scan
     // gives the run offsets; the thread whose run holds this item finds it.
     __shared__ int sWave[4], sItem[2];
@@ -122,7 +122,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
       before += u < w ? sWave[u] : 0;
       total += sWave[u];
     }
-    if (item >= total) return;  // past the last live split (uniform)
+    if ((int)blockIdx.x >= p.Hkv * p.hchunks * total) return;  // past the last live split (uniform)
+    gh = (int)blockIdx.x / total;
+    item = (int)blockIdx.x % total;
     const int excl = before + inc - cnt;
     if (item >= excl && item < excl + cnt) {
       int acc = excl;
@@ -140,6 +142,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
     b = __builtin_amdgcn_readfirstlane(sItem[0]);
     s = __builtin_amdgcn_readfirstlane(sItem[1]);
   } else {
+    const int per_gh = p.B * p.nsplit;
+    gh = blockIdx.x / per_gh;
+    item = blockIdx.x % per_gh;
     s = item % p.nsplit;
     b = item / p.nsplit;
   }
