@@ -321,7 +321,7 @@ def main():
         # ------------------------------------------------------------------ practical ceilings
         C = ctypes.CDLL(os.path.join(ROOT, "attention_fa_prefill_amd", "libfa_ceiling.so"))
         C.fa_ceiling_read.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
-        C.fa_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        C.fa_ceiling_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         rbuf = torch.ones(1 << 27, dtype=torch.float32, device=dev)  # 512 MiB
         rbytes = rbuf.numel() * 4
         sink = torch.zeros(1 << 16, dtype=torch.int32, device=dev)
@@ -334,12 +334,13 @@ def main():
         mm_grid, mm_rounds = 512, 1000
         mm_flop = mm_grid * 4 * 8 * mm_rounds * 32768
 
-        def mfma_call():
-            if C.fa_ceiling_mfma(ctypes.c_void_p(sink.data_ptr()), mm_grid, mm_rounds, ctypes_stream) != 0:
+        def mfma_call(normal):
+            if C.fa_ceiling_mfma(ctypes.c_void_p(sink.data_ptr()), mm_grid, mm_rounds, normal, ctypes_stream) != 0:
                 raise RuntimeError("ceiling mfma kernel launch failed")
 
         t_rd = statistics.median(timed_calls(read_call, 20, evict=True))
-        t_mm = statistics.median(timed_calls(mfma_call, 10, evict=False))
+        t_mm = statistics.median(timed_calls(lambda: mfma_call(0), 10, evict=False))
+        t_mn = statistics.median(timed_calls(lambda: mfma_call(1), 10, evict=False))
         del rbuf
         torch.cuda.empty_cache()
         result["ceilings"] = {
@@ -347,8 +348,11 @@ def main():
             "stream_read_frac_of_hbm_peak": round(rbytes / (t_rd * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "mfma_loop_bf16_TFLOP_per_s": round(mm_flop / (t_mm * 1e-6) / 1e12, 1),
             "mfma_loop_frac_of_bf16_peak": round(mm_flop / (t_mm * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "note": "plain 512 MiB streaming read (caches evicted) and an 8-chain v_mfma_f32_32x32x16_bf16 loop, "
-                    "timed per call with HIP events like the attention calls"}
+            "mfma_loop_bf16_normal_data_TFLOP_per_s": round(mm_flop / (t_mn * 1e-6) / 1e12, 1),
+            "mfma_loop_normal_data_frac_of_bf16_peak": round(mm_flop / (t_mn * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "note": "plain 512 MiB streaming read (caches evicted) and an 8-chain v_mfma_f32_32x32x16_bf16 loop on "
+                    "small integer operands and on N(0,1)-like bf16 operands (the matrix core's power, and so the "
+                    "clock, depends on the operand bits), timed per call with HIP events like the attention calls"}
 
     # ------------------------------------------------------------------ CPU baseline: the oracle
     if not args.no_cpu_baseline:
