@@ -9,8 +9,11 @@
 // the splits here are combined by log-sum-exp.
 //
 // Split kernel: one work-group (4 waves) per (sequence b, kv head g, group of
-// up to 16 query heads sharing g, split s of tps tokens), live splits numbered
-// densely so that the XCDs get equal shares of a mixed-length batch. Waves take 32-token
+// up to 16 query heads sharing g, split s of T tokens), live splits numbered
+// densely so that the XCDs get equal shares of a mixed-length batch. T is the
+// caller's split size, or with the default one of a few sizes chosen from
+// seqlens on the device, so that the live splits fill whole rounds of
+// resident work-groups. Waves take 32-token
 // steps round-robin and keep two steps of loads in flight. Per step:
 //   - K rows go HBM -> VGPRs directly in the A-operand layout of
 //     v_mfma_f32_16x16x32_bf16 (16 tokens x 32 dims per MFMA);
@@ -60,7 +63,10 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int kMaxPages = 128;           // pages per split (tps <= 2048)
+constexpr int kMaxTps = 2048;            // tokens per split at most
+constexpr int kMaxPages = kMaxTps / 16;  // pages per split
+constexpr int kCand = 4;                 // default split sizes tried: tps * {4, 5, 6, 8} / 4
+__host__ __device__ constexpr int cand_quarters(int u) { return u == 3 ? 8 : 4 + u; }
 constexpr int kPageSlots = kMaxPages + 32;  // + the pages of the loads issued past the end
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -68,6 +74,20 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP: shifts by 1, 2,
+// 4 and 8 lanes inside each row of 16 (lanes shifted in from outside the row
+// add 0), then the last lane of row 0 (of row 2) is added to row 1 (to row 3)
+// and the last lane of row 1 to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31, rows 2 and 3
+  return x;
 }
 
 template <int D>
@@ -89,9 +109,10 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   // blockIdx.x = gh * (splits per gh) + item: one block of work-groups per
   // (kv head, query-head chunk) pair gh, the splits of all sequences inside it.
   int gh, item;
+  int T = p.tps;  // tokens per split of this call
   auto splits_of = [&](int l) __attribute__((always_inline)) {
     l = l < 0 ? 0 : (l > p.max_len ? p.max_len : l);
-    return (l + p.tps - 1) / p.tps;
+    return (l + T - 1) / T;
   };
   int b, s;
   if (p.compact) {
@@ -103,30 +124,74 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
     // exit at once.
     // Each thread counts the splits of a run of sequences; a block-wide scan
     // gives the run offsets; the thread whose run holds this item finds it.
-    __shared__ int sWave[4], sItem[2];
+    //
+    // With the default split size the counts (and scans) are taken for
+    // tps * {1, 5/4, 3/2, 2} (multiples of 32, at most kMaxTps) in the same
+    // pass, and the size with the fewest tokens per work-group slot over the
+    // rounds of resident work-groups its live splits need wins (the smaller on
+    // a tie): a batch whose splits overrun one round by a few then runs in one
+    // round of slightly longer splits instead of two.
+    __shared__ int sWave[4][kCand], sItem[2];
     const int C = (p.B + 255) / 256;
     const int b0 = tid * C, b1 = min(p.B, b0 + C);
-    int cnt = 0;
-    for (int bb = b0; bb < b1; ++bb) cnt += splits_of(p.lens[bb]);
-    int inc = cnt;
+    int cand[kCand], cnt[kCand], inc[kCand];
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int y = __shfl_up(inc, off);
-      if (lane >= off) inc += y;
+    for (int u = 0; u < kCand; ++u) {
+      cand[u] = u == 0 ? p.tps : min(kMaxTps, (p.tps * cand_quarters(u) / 4 + kStep - 1) / kStep * kStep);
+      cnt[u] = 0;
     }
-    if (lane == 63) sWave[w] = inc;
+    for (int bb = b0; bb < b1; ++bb) {
+      int l = p.lens[bb];
+      l = l < 0 ? 0 : (l > p.max_len ? p.max_len : l);
+      cnt[0] += (l + cand[0] - 1) / cand[0];
+      if (p.adapt) {
+#pragma unroll
+        for (int u = 1; u < kCand; ++u) cnt[u] += (l + cand[u] - 1) / cand[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCand; ++u) {
+      inc[u] = (u > 0 && !p.adapt) ? cnt[u] : wave_inclusive_sum(cnt[u]);
+      if (lane == 63) sWave[w][u] = inc[u];
+    }
     __syncthreads();
+    int cs = 0;  // the candidate taken
+    if (p.adapt) {
+      // uniform values: scalar arithmetic (the grid of any candidate fits in
+      // 32 bits: it is at most the grid at tps, which the host checked)
+      unsigned long long best = ~0ull;
+#pragma unroll
+      for (int u = 0; u < kCand; ++u) {
+        const unsigned n = (unsigned)(p.Hkv * p.hchunks) *
+                           (unsigned)__builtin_amdgcn_readfirstlane(sWave[0][u] + sWave[1][u] + sWave[2][u] + sWave[3][u]);
+        const unsigned long long cost = (unsigned long long)((n + p.cap - 1) / (unsigned)p.cap) * (unsigned)cand[u];
+        if (cost < best) {
+          best = cost;
+          cs = u;
+        }
+      }
+    }
+    int mycnt = cnt[0], myinc = inc[0];
+    T = cand[0];
+#pragma unroll
+    for (int u = 1; u < kCand; ++u)
+      if (u == cs) {
+        mycnt = cnt[u];
+        myinc = inc[u];
+        T = cand[u];
+      }
+    if (blockIdx.x == 0 && tid == 0) *p.ws_t = T;  // read by the merge
     int before = 0, total = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      before += u < w ? sWave[u] : 0;
-      total += sWave[u];
+      before += u < w ? sWave[u][cs] : 0;
+      total += sWave[u][cs];
     }
     if ((int)blockIdx.x >= p.Hkv * p.hchunks * total) return;  // past the last live split (uniform)
     gh = (int)blockIdx.x / total;
     item = (int)blockIdx.x % total;
-    const int excl = before + inc - cnt;
-    if (item >= excl && item < excl + cnt) {
+    const int excl = before + myinc - mycnt;
+    if (item >= excl && item < excl + mycnt) {
       int acc = excl;
       for (int bb = b0; bb < b1; ++bb) {
         const int n = splits_of(p.lens[bb]);
@@ -141,7 +206,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
     __syncthreads();
     b = __builtin_amdgcn_readfirstlane(sItem[0]);
     s = __builtin_amdgcn_readfirstlane(sItem[1]);
+    if (b < 0 || b >= p.B || s < 0 || s >= p.nsplit) return;  // cannot happen: every live item has an owner
   } else {
+    if (blockIdx.x == 0 && tid == 0) *p.ws_t = T;  // read by the merge
     const int per_gh = p.B * p.nsplit;
     gh = blockIdx.x / per_gh;
     item = blockIdx.x % per_gh;
@@ -151,9 +218,9 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   const int g = gh / p.hchunks, hc = gh % p.hchunks;
   int len = p.lens[b];
   len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
-  const int tok0 = s * p.tps;
+  const int tok0 = s * T;
   if (tok0 >= len) return;  // empty split: the merge never reads it
-  const int tok1 = min(len, tok0 + p.tps);
+  const int tok1 = min(len, tok0 + T);
   const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
   const int hq0 = g * p.G + hc * 16;
   const int nh = min(16, p.G - hc * 16);
@@ -384,9 +451,11 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
   const int r = blockIdx.x, cb = blockIdx.y;
   int nS = p.S;
   if (p.lens) {
+    // the split kernel's split size (at least p.tps, so nS <= p.S)
+    const int T = p.tps_dev ? min(kMaxTps, max(p.tps, *p.tps_dev)) : p.tps;
     int len = p.lens[r / p.Hq];
     len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
-    nS = (len + p.tps - 1) / p.tps;
+    nS = min(p.S, (len + T - 1) / T);
   }
   const int c = tid % TPS, sg = tid / TPS;
   const float* lse = p.lse + (size_t)r * p.S;
@@ -481,6 +550,7 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) 
   m.S = p.nsplit;
   m.Hq = p.Hq;
   m.tps = p.tps;
+  m.tps_dev = p.ws_t;
   m.max_len = p.max_len;
   m.out_bf16 = 1;
   return launch_merge(m, d, stream);

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/fa.h"
 #include "fa_internal.h"
 
@@ -53,6 +55,22 @@ fa::PrefillParams make_prefill(const void* q, const void* k, const void* v, void
   p.nT = (Sq + 127) / 128;
   p.nP = (p.nT + 1) / 2;
   return p;
+}
+
+// Split work-groups resident at once on the current device: two per compute
+// unit (the split kernel's registers and LDS allow two). Cached per device.
+int resident_split_groups() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kTargetSplitGroups;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return kTargetSplitGroups;
+  v = 2 * cus;
+  cache[dev].store(v, std::memory_order_relaxed);
+  return v;
 }
 
 // Work-groups one split of every sequence launches: B * Hkv * ceil(G / 16).
@@ -118,7 +136,7 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, 
   if (d <= 0 || tps <= 0) return 0;
   const size_t nsplit = ((size_t)max_kv_len + tps - 1) / tps;
   const size_t rows = (size_t)B * Hq * nsplit;
-  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256) + 256;
 }
 
 fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
@@ -152,12 +170,15 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   p.G = G;
   p.hchunks = hchunks;
   p.compact = B <= kCompactMaxB ? 1 : 0;
+  p.adapt = (tokens_per_split == 0 && p.compact) ? 1 : 0;
+  p.cap = resident_split_groups();
   // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0
   p.c = fmaxf(fabsf(scale) * fa::kLog2e, 1e-30f);
   p.neg = scale < 0.f ? 1 : 0;
   const size_t rows = (size_t)B * Hq * p.nsplit;
   p.ws_o = (float*)workspace;
   p.ws_lse = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
+  p.ws_t = (int*)((char*)p.ws_lse + round_up(rows * sizeof(float), 256));
   return from_hip(fa::launch_decode_bf16(p, d, (hipStream_t)stream));
 }
 

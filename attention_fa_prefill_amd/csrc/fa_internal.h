@@ -51,6 +51,9 @@ struct DecodeParams {
   float c;             // |scale| * log2(e)
   int neg;
   int compact;         // number live splits densely (B small enough to scan per work-group)
+  int adapt;           // compact and default split size: the kernel may enlarge tps
+  int cap;             // split work-groups resident at once on this GPU
+  int* ws_t;           // the split size the split kernel used (written by work-group 0)
 };
 
 hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
@@ -60,7 +63,8 @@ struct MergeParams {
   const float* lse;      // [R, S] natural log
   void* o;               // [R, d] bf16 or fp32
   float* lse_out;        // [R] or nullptr
-  const int32_t* lens;   // if not null: valid splits of row r = ceil(clamp(lens[r / Hq]) / tps)
+  const int32_t* lens;   // if not null: valid splits of row r = ceil(clamp(lens[r / Hq]) / split size)
+  const int* tps_dev;    // if not null: the split size, in device memory (else tps)
   int R, S, Hq, tps, max_len, out_bf16;
 };
 

@@ -106,20 +106,28 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
 
 /*
  * fa_decode_split_tokens - the KV tokens each split work-group of fa_decode
- * covers (n_split = ceil(max_kv_len / result) splits per sequence).
+ * covers (n_split = ceil(max_kv_len / result) splits per sequence; this sizes
+ * the workspace).
  * tokens_per_split == 0 asks for the default: the smallest power of two in
  * [64, 1024] for which B * Hkv * ceil((Hq/Hkv)/16) * n_split stays near 512
  * work-groups (two per compute unit), so long sequences are split finely
  * enough to fill the GPU; 1024 keeps a 262144-token sequence at 256 splits.
+ * With the default and B <= 4096, fa_decode itself may then enlarge the split
+ * to 5/4, 3/2 or 2 times this value (a multiple of 32, at most 2048) once it
+ * sees seqlens on the device: it takes the size with the fewest tokens per
+ * work-group slot over the rounds of resident split work-groups (two per
+ * compute unit) that the live splits need, the smallest on a tie. Splits only
+ * get larger, so the workspace always suffices.
  * Any other value must be a positive multiple of 32, at most 2048, and is
- * returned unchanged. Returns 0 for invalid arguments.
+ * returned unchanged and used as given. Returns 0 for invalid arguments.
  */
 int fa_decode_split_tokens(int B, int Hq, int Hkv, int max_kv_len, int tokens_per_split);
 
 /*
  * fa_decode_workspace_bytes - bytes of device workspace fa_decode needs:
  * fp32 partial outputs [B, Hq, n_split, d] and partial log-sum-exps
- * [B, Hq, n_split], each rounded up to 256 bytes, with n_split as above.
+ * [B, Hq, n_split], each rounded up to 256 bytes, with n_split as above, then
+ * 256 bytes whose first int32 receives the split size the call used.
  * Returns 0 for invalid arguments.
  */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, int tokens_per_split);
@@ -149,8 +157,9 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, 
  *
  * Two kernels run in stream order: a split-KV kernel writing per-split
  * (normalised output, log-sum-exp), then the log-sum-exp merge into o.
- * For the same tokens_per_split the paged and contiguous paths perform the
- * same arithmetic in the same order, so their results are bitwise equal.
+ * For the same tokens_per_split and seqlens (the default split size depends on
+ * them) the paged and contiguous paths perform the same arithmetic in the same
+ * order, so their results are bitwise equal.
  */
 fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
                     const int32_t* block_table, const int32_t* seqlens, void* o,

@@ -99,17 +99,18 @@ def test_decode_split_tokens():
 
 
 def test_decode_workspace_bytes():
-    # [B, Hq, nsplit, d] fp32 partials + [B, Hq, nsplit] fp32 lse, each rounded up to 256 bytes
+    # [B, Hq, nsplit, d] fp32 partials + [B, Hq, nsplit] fp32 lse, each rounded up to 256 bytes,
+    # + 256 bytes for the split size the call used
     n = 32768 // 512
-    assert fa.decode_workspace_bytes(4, 32, 8, 128, 32768, 512) == 4 * 32 * n * 128 * 4 + 4 * 32 * n * 4
+    assert fa.decode_workspace_bytes(4, 32, 8, 128, 32768, 512) == 4 * 32 * n * 128 * 4 + 4 * 32 * n * 4 + 256
     t = fa.decode_split_tokens(4, 32, 8, 32768, 0)
     n = -(-32768 // t)
-    assert fa.decode_workspace_bytes(4, 32, 8, 128, 32768, 0) == 4 * 32 * n * 128 * 4 + 4 * 32 * n * 4
-    assert fa.decode_workspace_bytes(1, 1, 1, 64, 1, 32) == 256 + 256
+    assert fa.decode_workspace_bytes(4, 32, 8, 128, 32768, 0) == 4 * 32 * n * 128 * 4 + 4 * 32 * n * 4 + 256
+    assert fa.decode_workspace_bytes(1, 1, 1, 64, 1, 32) == 256 + 256 + 256
     assert fa.decode_workspace_bytes(0, 1, 1, 64, 1, 32) == 0
     assert fa.decode_workspace_bytes(1, 8, 3, 64, 64, 32) == 0
     n5 = -(-262144 // fa.decode_split_tokens(1, 16, 2, 262144, 0))
-    assert fa.decode_workspace_bytes(1, 16, 2, 128, 262144, 0) == 16 * n5 * 128 * 4 + 16 * n5 * 4
+    assert fa.decode_workspace_bytes(1, 16, 2, 128, 262144, 0) == 16 * n5 * 128 * 4 + 16 * n5 * 4 + 256
 
 
 @pytest.mark.parametrize("kw,code", [

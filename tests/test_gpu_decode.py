@@ -209,3 +209,46 @@ def test_merge_rejects_page_sum():
     ls = np.random.default_rng(28).standard_normal((2, S)).astype(np.float32)
     o, _ = fa.merge_lse(dev_f32(op), dev_f32(ls), out_dtype=torch.float32)
     assert np.max(np.abs(host_f64(o) - u)) < 1e-6
+
+
+def _default_split_size(case, t0, cap):
+    """The split size fa_decode picks on the device with tokens_per_split = 0:
+    of t0 * {1, 5/4, 3/2, 2} (multiples of 32, at most 2048), the one with the
+    fewest tokens per resident work-group slot over the rounds the live splits
+    need, the smallest on a tie."""
+    G = case.Hq // case.Hkv
+    gh = case.Hkv * -(-G // 16)
+    lens = np.clip(np.asarray(case.seqlens, dtype=np.int64), 0, case.max_kv_len)
+    best = None
+    for q4 in (4, 5, 6, 8):
+        t = min(2048, -(-(t0 * q4 // 4) // 32) * 32)
+        n = gh * int(np.sum(-(-lens // t)))
+        cost = -(-n // cap) * t
+        if best is None or cost < best[0]:
+            best = (cost, t)
+    return best[1]
+
+
+@pytest.mark.parametrize("make", [workloads.decode_contig_32k, workloads.decode_paged_mixed,
+                                  workloads.decode_long_256k])
+def test_default_split_size_chosen_on_device(make):
+    """With the default split size the kernel picks its split size from seqlens;
+    the size it reports in the workspace follows the documented rule, and the
+    output is bit for bit the output of an explicit call with that size."""
+    torch = torch_gpu()
+    case = make()
+    q, kc, vc = dev_bf16(case.q), dev_bf16(case.kcache), dev_bf16(case.vcache)
+    lens = dev_i32(case.seqlens)
+    bt = dev_i32(case.block_table) if case.paged else None
+    t0 = fa.decode_split_tokens(case.B, case.Hq, case.Hkv, case.max_kv_len, 0)
+    need = fa.decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.d, case.max_kv_len, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    print(f"case {case.name} default split size, t0={t0}", flush=True)
+    o_auto = fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=case.max_kv_len, scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    used = int(ws[need - 256:need - 252].view(torch.int32).item())
+    cap = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    assert used == _default_split_size(case, t0, cap)
+    o_explicit = fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=case.max_kv_len, scale=case.scale,
+                           tokens_per_split=used)
+    assert np.array_equal(host_bits(o_auto), host_bits(o_explicit))
