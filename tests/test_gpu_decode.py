@@ -211,6 +211,14 @@ def test_merge_rejects_page_sum():
     assert np.max(np.abs(host_f64(o) - u)) < 1e-6
 
 
+def _split_size_offset(case, t0):
+    """Byte offset of the split-size slot in the workspace: after the fp32
+    partials [B, Hq, n, d] and their lse [B, Hq, n], each rounded up to 256."""
+    r = lambda x: -(-x // 256) * 256
+    rows = case.B * case.Hq * -(-case.max_kv_len // t0)
+    return r(rows * case.d * 4) + r(rows * 4)
+
+
 def _default_split_size(case, t0, cap):
     """The split size fa_decode picks on the device with tokens_per_split = 0:
     of t0 * {1, 5/4, 3/2, 2} (multiples of 32, at most 2048), the one with the
@@ -246,9 +254,74 @@ def test_default_split_size_chosen_on_device(make):
     print(f"case {case.name} default split size, t0={t0}", flush=True)
     o_auto = fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=case.max_kv_len, scale=case.scale, workspace=ws)
     torch.cuda.synchronize()
-    used = int(ws[need - 256:need - 252].view(torch.int32).item())
+    used = int(ws[_split_size_offset(case, t0):][:4].view(torch.int32).item())
     cap = 2 * torch.cuda.get_device_properties(0).multi_processor_count
     assert used == _default_split_size(case, t0, cap)
     o_explicit = fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=case.max_kv_len, scale=case.scale,
                            tokens_per_split=used)
     assert np.array_equal(host_bits(o_auto), host_bits(o_explicit))
+
+
+def test_many_splits_and_empty_sequence():
+    """66, 22, 0 and 2 splits of 32 tokens in one batch (an empty sequence
+    gives o = 0)."""
+    lens = np.array([2100, 700, 0, 33], np.int32)
+    case = workloads.decode_paged(4, 8, 2, 128, lens, 2112, seed=41)
+    o = run(case, 32)
+    got = host_f64(o)
+    assert np.all(got[2] == 0.0)
+    assert_bf16_close(got, oracle_out(case), "many splits")
+
+
+def test_workspace_needs_no_initialisation():
+    """A workspace of random bytes works, and calls with other lengths on the
+    same workspace follow."""
+    torch = torch_gpu()
+    L = 1536
+    need = fa.decode_workspace_bytes(4, 8, 2, 128, L, 32)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda")
+    for i, lens in enumerate(([1500, 1, 700, 64], [33, 1536, 0, 900], [1500, 1, 700, 64])):
+        case = workloads.decode_paged(4, 8, 2, 128, np.array(lens, np.int32), L, seed=50 + i)
+        print(f"call {i} lens={lens}", flush=True)
+        o = fa.decode(dev_bf16(case.q), dev_bf16(case.kcache), dev_bf16(case.vcache), dev_i32(case.seqlens),
+                      block_table=dev_i32(case.block_table), max_kv_len=L, scale=case.scale, tokens_per_split=32,
+                      workspace=ws)
+        assert_bf16_close(host_f64(o), oracle_out(case), f"call {i}")
+
+
+def test_graph_capture_replays():
+    """fa_decode (split kernel, then merge kernel) captured in a HIP graph:
+    every replay, with eager work and synchronisations between replays and new
+    lengths written into seqlens in place, equals the eager call on the same
+    inputs bit for bit."""
+    torch = torch_gpu()
+    case = workloads.decode_paged_mixed()
+    q, kc, vc = dev_bf16(case.q), dev_bf16(case.kcache), dev_bf16(case.vcache)
+    lens = dev_i32(case.seqlens)
+    bt = dev_i32(case.block_table)
+    L = case.max_kv_len
+    need = fa.decode_workspace_bytes(case.B, case.Hq, case.Hkv, case.d, L, 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up on a side stream, as graph capture asks
+        fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=L, scale=case.scale, o=o, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=L, scale=case.scale, o=o, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for rep in range(4):
+        new_lens = case.seqlens if rep % 2 == 0 else rng.integers(0, L + 1, size=case.B).astype(np.int32)
+        lens.copy_(torch.from_numpy(np.ascontiguousarray(new_lens, dtype=np.int32)))
+        x = torch.randn(1 << 20, device="cuda")
+        (x * 2 + 1).sum().item()  # eager work between replays
+        print(f"replay {rep} lens={new_lens.tolist()}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        ref = fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=L, scale=case.scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(o), host_bits(ref)), f"replay {rep}"
