@@ -23,7 +23,7 @@ FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
 EXPORTS = ("fa_status_string", "fa_version", "fa_prefill", "fa_prefill_f32", "fa_decode_split_tokens",
-           "fa_decode_workspace_bytes", "fa_decode", "fa_merge_lse")
+           "fa_decode_workspace_bytes", "fa_decode", "fa_decode_fp8", "fa_merge_lse")
 
 _lib = None
 
@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.fa_decode_workspace_bytes.restype = sz
         L.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp, sz, vp]
         L.fa_decode.restype = ci
+        L.fa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, cf, cf, vp, sz, vp]
+        L.fa_decode_fp8.restype = ci
         L.fa_merge_lse.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, vp]
         L.fa_merge_lse.restype = ci
         _lib = L
@@ -154,11 +156,32 @@ def decode(q, kcache, vcache, seqlens, *, block_table=None, max_kv_len: int | No
     [num_pages, 16, Hkv, d]; max_kv_len defaults to 16 * pages_per_seq.
     Returns o [B,Hq,d] bf16.
     """
+    return _decode(q, kcache, vcache, seqlens, None, block_table, max_kv_len, scale, tokens_per_split, o, workspace,
+                   stream)
+
+
+def decode_fp8(q, kcache, vcache, seqlens, *, k_scale: float, v_scale: float, block_table=None,
+               max_kv_len: int | None = None, scale: float | None = None, tokens_per_split: int = 0, o=None,
+               workspace=None, stream=None):
+    """decode over an FP8 cache: kcache, vcache hold OCP FP8 E4M3 codes (uint8
+    or float8_e4m3fn tensors, same layouts as decode); K = k_scale * E4M3(code),
+    V = v_scale * E4M3(code). q and o bf16."""
+    return _decode(q, kcache, vcache, seqlens, (float(k_scale), float(v_scale)), block_table, max_kv_len, scale,
+                   tokens_per_split, o, workspace, stream)
+
+
+def _decode(q, kcache, vcache, seqlens, fp8_scales, block_table, max_kv_len, scale, tokens_per_split, o, workspace,
+            stream):
     torch = _torch()
     _dev(q, kcache, vcache, seqlens, block_table, o, workspace)
     _contig(q, kcache, vcache, seqlens, block_table, o, workspace)
-    if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
-        raise ValueError("decode takes bfloat16 q and caches")
+    if fp8_scales is None:
+        if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
+            raise ValueError("decode takes bfloat16 q and caches")
+    else:
+        byte_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
+        if q.dtype != torch.bfloat16 or kcache.dtype not in byte_types or vcache.dtype not in byte_types:
+            raise ValueError("decode_fp8 takes a bfloat16 q and uint8 / float8_e4m3fn caches")
     if seqlens.dtype != torch.int32 or (block_table is not None and block_table.dtype != torch.int32):
         raise ValueError("seqlens and block_table must be int32")
     B, Hq, d = q.shape
@@ -184,9 +207,13 @@ def decode(q, kcache, vcache, seqlens, *, block_table=None, max_kv_len: int | No
     need = decode_workspace_bytes(B, Hq, Hkv, d, mkl, tokens_per_split)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    check(lib().fa_decode(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens), _ptr(o), B, Hq,
-                          Hkv, d, mkl, page, int(tokens_per_split), float(scale), _ptr(workspace),
-                          workspace.numel() * workspace.element_size(), _stream_handle(q, stream)))
+    common = (_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens), _ptr(o), B, Hq, Hkv, d, mkl,
+              page, int(tokens_per_split), float(scale))
+    tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(q, stream))
+    if fp8_scales is None:
+        check(lib().fa_decode(*common, *tail))
+    else:
+        check(lib().fa_decode_fp8(*common, *fp8_scales, *tail))
     return o
 
 

@@ -36,6 +36,8 @@
 //
 // Merge kernel: per row, M = max lse_s, w_s = exp(lse_s - M),
 // o = sum_s w_s o_s / sum_s w_s, lse = M + log(sum_s w_s); empty splits skipped.
+#include <type_traits>
+
 #include "fa_internal.h"
 
 namespace fa {
@@ -50,16 +52,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // so the 4-row x 32-byte footprint of each transpose read hits distinct banks.
 template <int D>
 __device__ __forceinline__ int swz_v(int row) { return 2 * (row & (D == 128 ? 7 : 3)); }
+// FP8 V staging swizzle. A transpose read of 8-bit elements (ds_read_b64_tr_b8)
+// by 16 lanes covers one 16-byte chunk of 8 rows: tokens 4cq..4cq+3 and
+// 16+4cq..16+4cq+3 of the step. XOR with a function of the row that differs
+// on those 8 rows (D=128: 8 chunks per row) or, with the row's parity, still
+// separates them (D=64: 4 chunks per 64-byte row) places the 8 reads in
+// distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_v8(int row) {
+  return D == 128 ? ((row & 3) | (((row >> 4) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 4) & 1) << 1));
+}
 
 // Waits for this wave's vector-memory loads (direct-to-LDS included) until at
 // most N are outstanding. The memory clobber keeps LDS reads of a stage from
 // being scheduled above the wait that covers that stage's loads.
 template <int N>
 __device__ __forceinline__ void wait_vm() {
-  static_assert(N == 0 || N == 8 || N == 16, "wait count");
-  if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
@@ -71,9 +81,21 @@ constexpr int kPageSlots = kMaxPages + 32;  // + the pages of the loads issued p
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
+
+// 8 OCP FP8 E4M3 codes (byte i of x = element i) -> 8 bf16, exactly (every
+// E4M3 value is a bf16 value); the per-tensor scale is applied elsewhere.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 x) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave, on DPP: shifts by 1, 2,
@@ -90,15 +112,23 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
   return x;
 }
 
-template <int D>
+// F8: the cache holds OCP FP8 E4M3 codes (one byte per element) with one
+// scale per tensor: K = p.ks * code, V = p.vs * code. p.ks is folded into the
+// softmax factor c by the host and p.vs is applied to each split's output;
+// K and V are widened to bf16 exactly, so the arithmetic is that of the bf16
+// cache on the dequantised values.
+template <int D, bool F8>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
+  constexpr int ES = F8 ? 1 : 2;     // bytes per cached element
   constexpr int KS = D / 32;         // k-steps of S^T = K . Q^T (16x16x32)
   constexpr int DB = D / 16;         // 16-dim blocks of O^T
-  constexpr int CH = D / 8;          // 16-byte chunks per row
-  constexpr int RI = 64 / CH;        // V rows per direct-to-LDS load (4 for D=128)
+  constexpr int CH = D * ES / 16;    // 16-byte chunks per row
+  constexpr int RI = 64 / CH;        // V rows per direct-to-LDS load (bf16 D=128: 4; fp8: 8)
   constexpr int VDMA = kStep / RI;   // direct-to-LDS loads per step
   constexpr int NLD = 2 * KS + VDMA; // vector-memory instructions issued per step
-  // Two V stages per wave (the step being used and the one in flight).
+  // Two V stages per wave (the step being used and the one in flight); an
+  // FP8 step uses the first half of a stage. sV0 doubles as the exchange of
+  // the 4 waves' states at the end.
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[4][kStep * D];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[4][kStep * D];
   __shared__ float sM[4][64], sL[4][64];
@@ -254,25 +284,37 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   // Buffer resource over page pi (relative to the split) of kv head g: its
   // record count ends right after the last valid token row, so rows past the
   // sequence length read as zero (K: masked score; V: no NaN can leak).
-  const size_t rowstride = (size_t)Hkv * D * 2;  // bytes between consecutive tokens
+  const size_t rowstride = (size_t)Hkv * D * ES;  // bytes between consecutive tokens
   auto page_rsrc = [&](const void* cache, int pi) __attribute__((always_inline)) {
     const int nvalid = max(0, min(16, tok1 - (tok0 + 16 * pi)));
     const int row0 = __builtin_amdgcn_readfirstlane(sRow0[pi]);
-    const char* base = (const char*)cache + ((size_t)row0 * Hkv + g) * (size_t)(D * 2);
-    const int nrec = max(0, (nvalid - 1) * (int)rowstride + D * 2);
+    const char* base = (const char*)cache + ((size_t)row0 * Hkv + g) * (size_t)(D * ES);
+    const int nrec = max(0, (nvalid - 1) * (int)rowstride + D * ES);
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kRsrcWord3);
   };
   // K operand of one 32-token step: half h = page 2st+h, lane (n, cq) holds
   // K[token n of the page][32 ks + 8 cq .. +8] - the A layout of 16x16x32.
-  const int koff = (int)((size_t)n * rowstride) + 16 * cq;
-  auto load_k = [&](int st, u32x4 (&kb)[2][KS]) __attribute__((always_inline)) {
+  // (FP8: 8 bytes of codes per lane, widened at use.)
+  using KReg = typename std::conditional<F8, u32x2, u32x4>::type;
+  const int koff = (int)((size_t)n * rowstride) + 8 * ES * cq;
+  auto load_k = [&](int st, KReg (&kb)[2][KS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.kc, 2 * st + h);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kb[h][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff + 64 * ks, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (F8)
+          kb[h][ks] = __builtin_amdgcn_raw_buffer_load_b64(rs, koff + 32 * ks, 0, 0);
+        else
+          kb[h][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, koff + 64 * ks, 0, 0);
+      }
     }
+  };
+  auto k_operand = [&](const KReg& x) __attribute__((always_inline)) {
+    if constexpr (F8)
+      return fp8x8_to_bf16(x);
+    else
+      return __builtin_bit_cast(bf16x8, x);
   };
   // V rows of one step -> this wave's LDS stage, 16 bytes per lane per load;
   // LDS chunk pc of row r holds logical chunk pc ^ swz(r).
@@ -282,7 +324,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
       const int r = ii * RI + lane / CH, pc = lane % CH;
       const int h = (ii * RI) / 16;  // page of this load (uniform)
       const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.vc, 2 * st + h);
-      const int voff = (int)((size_t)(r & 15) * rowstride) + ((pc ^ swz_v<D>(r)) << 4);
+      const int sw = F8 ? swz_v8<D>(r) : swz_v<D>(r);
+      const int voff = (int)((size_t)(r & 15) * rowstride) + ((pc ^ sw) << 4);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + ii * 64 * 8), 16, voff, 0, 0, 0);
     }
   };
@@ -291,20 +334,26 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) O[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  const float c = p.c;
+  const float c = p.c;  // FP8: includes the K scale
   const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
   const int y = lane & 15;
   const int row1 = 4 * cq + (y >> 2), row2 = 16 + 4 * cq + (y >> 2);
 
   // One 32-token step from K registers kb and V stage `stage`.
-  auto step = [&](int st, const u32x4 (&kb)[2][KS], const __bf16* stage) __attribute__((always_inline)) {
+  // FP8 V^T operand: lane (cq, j) supplies half j % 2 of chunk db of row
+  // t(j / 2), and the transpose read returns to lane j column j of the chunk
+  // over those 8 rows, i.e. 8 tokens of dim 16 db + j in the order the score
+  // registers hold them.
+  const int rho = (lane & 15) >> 1;
+  const int trow = rho < 4 ? 4 * cq + rho : 16 + 4 * cq + (rho - 4);
+  auto step = [&](int st, const KReg (&kb)[2][KS], const __bf16* stage) __attribute__((always_inline)) {
     const int tb = tok0 + st * kStep;
     f32x4 S[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       S[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) S[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kb[h][ks]), qop[ks], S[h], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) S[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k_operand(kb[h][ks]), qop[ks], S[h], 0, 0, 0);
     }
     // S^T lane (n, cq) reg r is token tb + 16 h + 4 cq + r of head n; tokens
     // past the end get -inf (their K rows read as zero).
@@ -346,6 +395,15 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
     // O^T += V^T . P^T; contraction index 8 cq + i is token 4 cq + i (i < 4)
     // or 16 + 4 cq + (i - 4) (i >= 4), matching the score registers.
     const char* vslot = (const char*)stage;
+    if constexpr (F8) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const char* a8 = vslot + trow * D + ((db ^ swz_v8<D>(trow)) << 4) + 8 * (lane & 1);
+        const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)a8);
+        O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(__builtin_bit_cast(u32x2, v8)), pop, O[db], 0, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int colb = (16 * db + 4 * (y & 3)) * 2;
@@ -365,7 +423,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   const int nw = nsteps > w ? (nsteps - w + 3) / 4 : 0;
   // kept as raw dwords: a bf16-typed copy across the loop makes the compiler
   // repack the halves, which waits for the loads right after they are issued
-  u32x4 kA[2][KS], kB[2][KS];
+  KReg kA[2][KS], kB[2][KS];
   __bf16* stA = sV0[w];
   __bf16* stB = sV1[w];
   dma_v(w, stA);
@@ -423,7 +481,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
         float x = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) x += a[u] * ((const float*)sV0[u])[(db * 4 + r) * 64 + lane];
-        acc[r] = x * inv;
+        acc[r] = x * inv * p.vs;
       }
       *(float4*)(dst + 16 * db + 4 * cq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
@@ -532,12 +590,16 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream) {
   dim3 grid(p.B * p.nsplit * p.Hkv * p.hchunks), block(256);
-  if (d == 128)
-    hipLaunchKernelGGL(decode_split_kernel<128>, grid, block, 0, stream, p);
+  if (d == 128 && !fp8)
+    hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, block, 0, stream, p);
+  else if (d == 64 && !fp8)
+    hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, block, 0, stream, p);
+  else if (d == 128)
+    hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(decode_split_kernel<64>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeParams m;

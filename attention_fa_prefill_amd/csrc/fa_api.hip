@@ -139,9 +139,16 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, 
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256) + 256;
 }
 
-fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
-                    const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
-                    int tokens_per_split, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// fa_decode and fa_decode_fp8: the same checks and plan; fp8 caches carry a
+// positive finite scale per tensor.
+fa_status decode_common(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                        const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
+                        int tokens_per_split, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (!q || !kcache || !vcache || !seqlens || !o) return FA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_kv_len <= 0) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
@@ -150,6 +157,7 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   const int tps = fa_decode_split_tokens(B, Hq, Hkv, max_kv_len, tokens_per_split);
   if (tps <= 0) return FA_ERR_ARG;
   if (!isfinite(scale)) return FA_ERR_ARG;
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o)) return FA_ERR_ALIGN;
   if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
   const int G = Hq / Hkv;
@@ -172,14 +180,35 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
   p.compact = B <= kCompactMaxB ? 1 : 0;
   p.adapt = (tokens_per_split == 0 && p.compact) ? 1 : 0;
   p.cap = resident_split_groups();
-  // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0
-  p.c = fmaxf(fabsf(scale) * fa::kLog2e, 1e-30f);
+  // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0;
+  // an fp8 K scale multiplies every score, so it joins c
+  p.c = fmaxf(fabsf(scale) * (fp8 ? k_scale : 1.0f) * fa::kLog2e, 1e-30f);
+  p.vs = fp8 ? v_scale : 1.0f;
   p.neg = scale < 0.f ? 1 : 0;
   const size_t rows = (size_t)B * Hq * p.nsplit;
   p.ws_o = (float*)workspace;
   p.ws_lse = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
   p.ws_t = (int*)((char*)p.ws_lse + round_up(rows * sizeof(float), 256));
-  return from_hip(fa::launch_decode_bf16(p, d, (hipStream_t)stream));
+  return from_hip(fa::launch_decode(p, d, fp8, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                    const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
+                    int tokens_per_split, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_common(q, kcache, vcache, block_table, seqlens, o, B, Hq, Hkv, d, max_kv_len, page_size,
+                       tokens_per_split, scale, false, 1.0f, 1.0f, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                        const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
+                        int tokens_per_split, float scale, float k_scale, float v_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return decode_common(q, kcache, vcache, block_table, seqlens, o, B, Hq, Hkv, d, max_kv_len, page_size,
+                       tokens_per_split, scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* lse_out, int R, int S, int d,

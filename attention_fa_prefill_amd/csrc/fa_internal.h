@@ -38,7 +38,7 @@ hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream)
 // ---------------------------------------------------------------- decode
 struct DecodeParams {
   const void* q;       // bf16 [B, Hq, d]
-  const void* kc;      // bf16 rows of [*, Hkv, d]
+  const void* kc;      // bf16 (or FP8 E4M3) rows of [*, Hkv, d]
   const void* vc;
   const int32_t* bt;   // block table or nullptr
   const int32_t* lens; // [B]
@@ -48,7 +48,8 @@ struct DecodeParams {
   int B, Hq, Hkv, max_len, pages_per_seq, tps, nsplit;
   int G;               // query heads per kv head
   int hchunks;         // ceil(G / 16)
-  float c;             // |scale| * log2(e)
+  float c;             // |scale| * log2(e) (FP8 cache: times the K scale)
+  float vs;            // V scale (FP8 cache), 1 for bf16
   int neg;
   int compact;         // number live splits densely (B small enough to scan per work-group)
   int adapt;           // compact and default split size: the kernel may enlarge tps
@@ -56,7 +57,8 @@ struct DecodeParams {
   int* ws_t;           // the split size the split kernel used (written by work-group 0)
 };
 
-hipError_t launch_decode_bf16(const DecodeParams& p, int d, hipStream_t stream);
+// fp8: kc / vc hold OCP FP8 E4M3 codes (K = c-folded scale * code, V = vs * code)
+hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream);
 
 struct MergeParams {
   const float* o_parts;  // [R, S, d]

@@ -168,6 +168,29 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_fp8 - fa_decode over a KV cache stored as 8-bit floats, one byte
+ * per element: the low-precision KV cache of the FasterTransformer source
+ * walkthrough (section 3.3, an 8-bit KV cache that halves the bytes a decode
+ * step reads) in the FP8 form of the FlashRT project summary (8-bit floating
+ * point with one scale per tensor).
+ *
+ *   kcache, vcache : uint8 OCP FP8 E4M3 codes (bias 7, no infinities, codes
+ *                    0x7F / 0xFF are NaN) in the layouts of fa_decode;
+ *                    element value = k_scale * E4M3(code) for K and
+ *                    v_scale * E4M3(code) for V.
+ *   k_scale, v_scale : finite and > 0, else FA_ERR_ARG.
+ *   Every other argument, the workspace (same size and use) and the errors
+ *   are those of fa_decode; q and o stay bf16. K and V are widened to bf16
+ *   exactly (every E4M3 value is a bf16 value), so the result is that of
+ *   fa_decode on the dequantised cache up to the rounding of the scales.
+ */
+fa_status fa_decode_fp8(const void* q, const void* kcache, const void* vcache,
+                        const int32_t* block_table, const int32_t* seqlens, void* o,
+                        int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
+                        int tokens_per_split, float scale, float k_scale, float v_scale,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_merge_lse - combine R rows of S partial attention results by
  * log-sum-exp (the merge step that replaces the per-page sum of the paged
  * sketch on the real-time inference page):

@@ -135,6 +135,34 @@ def decode(q, kcache, vcache, seqlens, scale: float, block_table=None, page_size
     return o, lse
 
 
+def e4m3_to_f64(codes) -> np.ndarray:
+    """OCP 8-bit floating point E4M3 (the "FN" variant: no infinities) to
+    fp64, from the definition of the format: bit 7 sign, bits 6..3 exponent
+    field E with bias 7, bits 2..0 mantissa field M. E = 0 is subnormal,
+    (M / 8) * 2^-6; E = 15 with M = 7 is NaN; otherwise (1 + M / 8) * 2^(E - 7).
+    The largest finite value is 448 (E = 15, M = 6). This is the 8-bit KV-cache
+    element of the fp8 decode (FasterTransformer walkthrough, section 3.3: an
+    8-bit KV cache; FlashRT summary: FP8 with one scale per tensor)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (c & 7 == 7), np.nan, mag)
+    return sign * mag
+
+
+def decode_fp8(q, kcodes, vcodes, seqlens, scale: float, k_scale: float, v_scale: float, block_table=None,
+               page_size: int = 16, max_kv_len=None, lib: str | None = None):
+    """decode over an FP8 E4M3 cache with one scale per tensor: the cache is
+    dequantised (K = k_scale * E4M3(code), V = v_scale * E4M3(code)) and the
+    same definition applied in fp64. Returns (o [B, Hq, d], lse [B, Hq])."""
+    kc = e4m3_to_f64(kcodes) * float(k_scale)
+    vc = e4m3_to_f64(vcodes) * float(v_scale)
+    return decode(q, kc, vc, seqlens, scale, block_table=block_table, page_size=page_size, max_kv_len=max_kv_len,
+                  lib=lib)
+
+
 def merge(o_parts, lse_parts, lib: str | None = None):
     """Log-sum-exp merge. o_parts [R, S, d] (normalised parts), lse_parts [R, S].
     Returns (o [R, d], lse [R])."""

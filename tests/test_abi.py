@@ -77,6 +77,27 @@ def test_decode_rejects(kw, code):
     assert decode(**kw) == code
 
 
+def decode_fp8(ks=0.5, vs=0.5, **kw):
+    a = dict(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, page=16, tps=0, scale=0.1, ws=A,
+             wsb=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = fa.decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["d"], a["L"], a["tps"]) if a["B"] > 0 else 0
+    return fa.lib().fa_decode_fp8(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["o"], a["B"], a["Hq"], a["Hkv"],
+                                  a["d"], a["L"], a["page"], a["tps"], a["scale"], ks, vs, a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ks=0.0), ARG), (dict(ks=-1.0), ARG), (dict(ks=float("nan")), ARG), (dict(ks=float("inf")), ARG),
+    (dict(vs=0.0), ARG), (dict(vs=-0.5), ARG), (dict(vs=float("nan")), ARG), (dict(vs=float("inf")), ARG),
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(d=96), UNSUP), (dict(Hq=6, Hkv=4), SHAPE),
+    (dict(tps=48), ARG), (dict(k=A + 8), ALIGN), (dict(wsb=16), WS),
+])
+def test_decode_fp8_rejects(kw, code):
+    """The fp8 entry point checks what fa_decode checks, and its scales (finite, > 0)."""
+    assert decode_fp8(**kw) == code
+
+
 def test_decode_split_tokens():
     # explicit sizes are returned unchanged, invalid ones give 0
     assert fa.decode_split_tokens(4, 32, 8, 32768, 256) == 256

@@ -325,3 +325,88 @@ def test_graph_capture_replays():
         ref = fa.decode(q, kc, vc, lens, block_table=bt, max_kv_len=L, scale=case.scale)
         torch.cuda.synchronize()
         assert np.array_equal(host_bits(o), host_bits(ref)), f"replay {rep}"
+
+
+# --------------------------------------------------------------------------- FP8 E4M3 cache
+
+
+def dev_u8(codes):
+    torch = torch_gpu()
+    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to("cuda")
+
+
+def run_fp8(case, tps=0):
+    torch_gpu()
+    print(f"case {case.name} paged={case.paged} tps={tps} ks={case.k_scale} vs={case.v_scale}", flush=True)
+    q, kc, vc = dev_bf16(case.q), dev_u8(case.kcache), dev_u8(case.vcache)
+    lens = dev_i32(case.seqlens)
+    bt = dev_i32(case.block_table) if case.paged else None
+    return fa.decode_fp8(q, kc, vc, lens, k_scale=case.k_scale, v_scale=case.v_scale, block_table=bt,
+                         max_kv_len=case.max_kv_len, scale=case.scale, tokens_per_split=tps)
+
+
+def oracle_out_fp8(case):
+    q = workloads.bf16_bits_to_f64(case.q)
+    o, _ = oracle.decode_fp8(q, case.kcache, case.vcache, case.seqlens, case.scale, case.k_scale, case.v_scale,
+                             block_table=case.block_table, max_kv_len=case.max_kv_len)
+    return o
+
+
+@pytest.mark.parametrize("make", [workloads.decode_contig_32k, workloads.decode_paged_mixed,
+                                  workloads.decode_long_256k])
+def test_fp8_full_size(make):
+    case = workloads.as_fp8(make())
+    o = run_fp8(case)
+    assert_bf16_close(host_f64(o), oracle_out_fp8(case), case.name)
+
+
+def test_fp8_paged_equals_contiguous_bitwise():
+    case = workloads.as_fp8(workloads.decode_contiguous(4, 16, 4, 128, 4096, seed=61))
+    paged = workloads.paged_from_contiguous(case)
+    assert paged.fp8
+    assert np.array_equal(host_bits(run_fp8(case)), host_bits(run_fp8(paged)))
+
+
+def test_fp8_equals_bf16_on_the_dequantised_cache():
+    """With power-of-two scales the dequantised cache is exact in bf16, the K
+    scale folds exactly into the softmax factor and the V scale into the
+    output: the fp8 path must give the bf16 path's result bit for bit."""
+    case = workloads.as_fp8(workloads.decode_paged_mixed(), k_scale=0.5, v_scale=0.25)
+    deq_k = workloads.f32_to_bf16_bits((oracle.e4m3_to_f64(case.kcache) * 0.5).astype(np.float32))
+    deq_v = workloads.f32_to_bf16_bits((oracle.e4m3_to_f64(case.vcache) * 0.25).astype(np.float32))
+    o8 = run_fp8(case)
+    o16 = fa.decode(dev_bf16(case.q), dev_bf16(deq_k), dev_bf16(deq_v), dev_i32(case.seqlens),
+                    block_table=dev_i32(case.block_table), max_kv_len=case.max_kv_len, scale=case.scale)
+    assert np.array_equal(host_bits(o8), host_bits(o16))
+
+
+@pytest.mark.parametrize("G,Hkv,d", [(1, 4, 128), (4, 2, 64), (8, 1, 128), (32, 1, 128), (5, 2, 64)])
+@pytest.mark.parametrize("tps", [0, 32, 1024])
+def test_fp8_head_groups_and_split_sizes(G, Hkv, d, tps):
+    lens = np.array([1, 16, 200, 1500], np.int32)
+    case = workloads.as_fp8(workloads.decode_paged(4, G * Hkv, Hkv, d, lens, 1536, seed=G * 100 + d + tps + 7))
+    o = run_fp8(case, tps)
+    assert_bf16_close(host_f64(o), oracle_out_fp8(case), f"{case.name} G={G} tps={tps}")
+
+
+@pytest.mark.parametrize("ks,vs,scale", [(0.02, 3.0, None), (4.0, 0.01, None), (0.35, 0.6, -0.09), (1.0, 1.0, 0.0)])
+def test_fp8_scales(ks, vs, scale):
+    base = workloads.decode_paged(3, 8, 2, 128, np.array([700, 33, 1], np.int32), 768, seed=71)
+    case = workloads.as_fp8(base, k_scale=ks, v_scale=vs)
+    if scale is not None:
+        case.scale = scale
+    o = run_fp8(case, 64)
+    assert_bf16_close(host_f64(o), oracle_out_fp8(case), f"ks={ks} vs={vs} scale={scale}")
+
+
+def test_fp8_poisoned_slots_do_not_leak():
+    """NaN codes in tail slots past each length and in unused pages: output
+    finite and equal to the unpoisoned run bit for bit."""
+    lens = np.array([1, 15, 16, 17, 31, 33, 100, 513], np.int32)
+    clean = workloads.as_fp8(workloads.decode_paged(8, 8, 2, 128, lens, 640, seed=21), seed=5)
+    dirty = workloads.as_fp8(workloads.decode_paged(8, 8, 2, 128, lens, 640, seed=21, poison=True), seed=5)
+    assert np.sum(dirty.kcache == workloads.FP8_NAN) > 0
+    o_clean, o_dirty = run_fp8(clean), run_fp8(dirty)
+    assert np.all(np.isfinite(host_f64(o_dirty)))
+    assert np.array_equal(host_bits(o_dirty), host_bits(o_clean))
+    assert_bf16_close(host_f64(o_dirty), oracle_out_fp8(clean), "fp8 poisoned")

@@ -24,6 +24,7 @@ size 16 as in the paged sketch of the real-time inference page):
 from __future__ import annotations
 
 import math
+import zlib
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -134,6 +135,9 @@ class DecodeCase:
     kcache: np.ndarray = field(repr=False)  # bf16 bits: [B,max_kv_len,Hkv,d] or pool [P,16,Hkv,d]
     vcache: np.ndarray = field(repr=False)
     block_table: np.ndarray | None = field(default=None, repr=False)  # int32 [B, ceil(max_kv_len/16)]
+    fp8: bool = False        # kcache / vcache hold uint8 OCP FP8 E4M3 codes
+    k_scale: float = 1.0     # per-tensor scales of an fp8 cache
+    v_scale: float = 1.0
 
     @property
     def paged(self) -> bool:
@@ -228,9 +232,43 @@ def paged_from_contiguous(case: DecodeCase, seed: int = 99) -> DecodeCase:
     P = B * pps
     perm = rng(seed, 5).permutation(P).astype(np.int32)
     bt = perm.reshape(B, pps)
-    kp = np.empty((P, PAGE, case.Hkv, case.d), dtype=np.uint16)
+    kp = np.empty((P, PAGE, case.Hkv, case.d), dtype=case.kcache.dtype)
     vp = np.empty_like(kp)
     kp[bt.reshape(-1)] = case.kcache.reshape(B * pps, PAGE, case.Hkv, case.d)
     vp[bt.reshape(-1)] = case.vcache.reshape(B * pps, PAGE, case.Hkv, case.d)
     return DecodeCase(case.name + "_paged", case.B, case.Hq, case.Hkv, case.d, L, case.scale,
-                      case.seqlens.copy(), case.q, kp, vp, bt)
+                      case.seqlens.copy(), case.q, kp, vp, bt, case.fp8, case.k_scale, case.v_scale)
+
+
+# --------------------------------------------------------------------------- fp8 KV cache
+
+FP8_NAN = 0x7F  # an OCP FP8 E4M3 NaN code
+
+
+def fp8_codes(seed: int, stream: int, shape) -> np.ndarray:
+    """Random OCP FP8 E4M3 codes (uint8), drawn as bit fields: sign uniform,
+    biased exponent field 3..8 with weights 1:2:4:6:5:2 (magnitudes 1/16 ..
+    3.75, most near 1/2 .. 2), mantissa field uniform 0..7, and 1 % zero codes.
+    Never a NaN code (exponent field 15 is not drawn)."""
+    g = rng(seed, stream)
+    n = int(np.prod(shape))
+    sign = g.integers(0, 2, size=n, dtype=np.uint8)
+    w = np.array([1, 2, 4, 6, 5, 2], dtype=np.float64)
+    expo = (3 + g.choice(6, size=n, p=w / w.sum())).astype(np.uint8)
+    mant = g.integers(0, 8, size=n, dtype=np.uint8)
+    codes = (sign << 7) | (expo << 3) | mant
+    codes[g.random(n) < 0.01] = 0
+    return codes.reshape(shape).astype(np.uint8)
+
+
+def as_fp8(case: DecodeCase, k_scale: float = 0.35, v_scale: float = 0.6, seed: int | None = None) -> DecodeCase:
+    """The same decode case (q, lengths, block table) over an FP8 E4M3 cache of
+    random codes with per-tensor scales; slots that hold NaN in the bf16 cache
+    (poisoned tails and pages) hold the NaN code."""
+    sd = (zlib.crc32(case.name.encode()) % 100000) if seed is None else seed
+    kc = fp8_codes(sd, 6, case.kcache.shape)
+    vc = fp8_codes(sd, 7, case.vcache.shape)
+    kc[case.kcache == BF16_NAN] = FP8_NAN
+    vc[case.vcache == BF16_NAN] = FP8_NAN
+    return DecodeCase(case.name + "_fp8", case.B, case.Hq, case.Hkv, case.d, case.max_kv_len, case.scale,
+                      case.seqlens.copy(), case.q, kc, vc, case.block_table, True, float(k_scale), float(v_scale))
