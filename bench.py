@@ -68,7 +68,8 @@ def decode_bytes(case):
     import numpy as np
 
     lens = np.clip(case.seqlens, 0, case.max_kv_len).astype(np.int64)
-    b = 2 * (2 * case.Hkv * case.d * int(lens.sum()) + 2 * case.B * case.Hq * case.d) + 4 * case.B
+    es = 1 if getattr(case, "fp8", False) else 2  # bytes per cached element (FP8 E4M3 or bf16)
+    b = es * 2 * case.Hkv * case.d * int(lens.sum()) + 2 * 2 * case.B * case.Hq * case.d + 4 * case.B
     if case.paged:
         b += 4 * int(((lens + 15) // 16).sum())
     return b
@@ -178,8 +179,15 @@ def main():
 
     def decode_leg():
         dec = {}
-        for dc in (workloads.decode_contig_32k(), workloads.decode_paged_mixed(), workloads.decode_long_256k()):
-            dq, dk, dv = bf16(dc.q), bf16(dc.kcache), bf16(dc.vcache)
+        makers = (workloads.decode_contig_32k, workloads.decode_paged_mixed, workloads.decode_long_256k)
+        cases = [m() for m in makers] + [workloads.as_fp8(m()) for m in makers]
+        for dc in cases:
+            if dc.fp8:  # FP8 E4M3 codes, one byte per element
+                dk = torch.from_numpy(np.ascontiguousarray(dc.kcache)).to(dev)
+                dv = torch.from_numpy(np.ascontiguousarray(dc.vcache)).to(dev)
+                dq = bf16(dc.q)
+            else:
+                dq, dk, dv = bf16(dc.q), bf16(dc.kcache), bf16(dc.vcache)
             lens = i32(dc.seqlens)
             bt = i32(dc.block_table) if dc.paged else None
             od = torch.empty_like(dq)
@@ -192,8 +200,11 @@ def main():
                      ctypes.c_void_p(od.data_ptr()), dc.B, dc.Hq, dc.Hkv, dc.d, dc.max_kv_len,
                      16 if dc.paged else 0, 0, dc.scale, ctypes.c_void_p(ws.data_ptr()), need, ctypes_stream)
 
-            def dcall(dargs=dargs):
-                st = L.fa_decode(*dargs)
+            def dcall(dargs=dargs, fp8=dc.fp8, ks=dc.k_scale, vs=dc.v_scale):
+                if fp8:
+                    st = L.fa_decode_fp8(*dargs[:14], ks, vs, *dargs[14:])
+                else:
+                    st = L.fa_decode(*dargs)
                 if st != 0:
                     raise RuntimeError(fa.status_string(st))
 
@@ -210,7 +221,12 @@ def main():
                             "us_per_call_p50_warm": round(statistics.median(t_warm), 2),
                             "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "d": dc.d, "tokens": dc.total_tokens(),
                             "paged": dc.paged, "tokens_per_split": tps,
-                            "splits_per_kv_head": int(sum(-(-min(int(x), dc.max_kv_len) // tps) for x in dc.seqlens))}
+                            "splits_per_kv_head": int(sum(-(-min(int(x), dc.max_kv_len) // tps) for x in dc.seqlens)),
+                            "kv_cache": "fp8_e4m3" if dc.fp8 else "bf16"}
+            if dc.fp8:
+                base = dec[dc.name[: -len("_fp8")]]
+                dec[dc.name]["k_scale"], dec[dc.name]["v_scale"] = dc.k_scale, dc.v_scale
+                dec[dc.name]["speedup_vs_bf16_cache"] = round(base["us_per_call_p50"] / p50, 3)
             del dq, dk, dv, ws, od, lens, bt
             torch.cuda.empty_cache()
         return dec
