@@ -309,6 +309,13 @@ def main():
                                      "unit": "GB/s", "frac": long["frac_of_hbm_peak"], "traffic": traffic_dec,
                                      "workload": "decode_long_b1h16x2kv256kd128",
                                      "note": "split + merge kernels per call, caches evicted (by a 1 GiB read) before each call"}
+        long8 = dec["decode_long_b1h16x2kv256kd128_fp8"]
+        result["roofline_decode_fp8"] = {
+            "bound": "hbm", "achieved": long8["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": long8["frac_of_hbm_peak"],
+            "traffic": traffic_for("decode_split_kernel<128, fp8>@decode_long_b1h16x2kv256kd128_fp8", DECODE_KERNEL_SRC),
+            "workload": "decode_long_b1h16x2kv256kd128_fp8",
+            "note": "FP8 E4M3 cache (1 byte per element); split + merge kernels per call, caches evicted before each call"}
 
         # fp32 single-head causal prefill at B=1 (launch-latency bound)
         c1 = workloads.prefill_f32_small()
