@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libfa.so")
 FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
-EXPORTS = ("fa_status_string", "fa_version", "fa_prefill", "fa_prefill_f32", "fa_decode_split_tokens",
+EXPORTS = ("fa_status_string", "fa_version", "fa_prefill", "fa_prefill_f32", "fa_prefill_cache", "fa_decode_split_tokens",
            "fa_decode_workspace_bytes", "fa_decode", "fa_decode_fp8", "fa_merge_lse")
 
 _lib = None
@@ -51,6 +51,8 @@ def lib() -> ctypes.CDLL:
         L.fa_prefill.restype = ci
         L.fa_prefill_f32.argtypes = pre
         L.fa_prefill_f32.restype = ci
+        L.fa_prefill_cache.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+        L.fa_prefill_cache.restype = ci
         L.fa_decode_split_tokens.argtypes = [ci, ci, ci, ci, ci]
         L.fa_decode_split_tokens.restype = ci
         L.fa_decode_workspace_bytes.argtypes = [ci, ci, ci, ci, ci, ci]
@@ -135,6 +137,45 @@ def prefill(q, k, v, o=None, *, causal: bool = True, scale: float | None = None,
     fn = lib().fa_prefill if q.dtype == torch.bfloat16 else lib().fa_prefill_f32
     check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), B, Hq, Hkv, Sq, Skv, d, float(scale), int(bool(causal)),
              _stream_handle(q, stream)))
+    return o
+
+
+def prefill_cache(q, kcache, vcache, seqlens, *, block_table=None, max_kv_len: int | None = None, causal: bool = True,
+                  scale: float | None = None, o=None, stream=None):
+    """Chunked prefill over a KV cache. q [B,Hq,Sq,d] bf16 (each sequence's Sq
+    new queries); kcache, vcache bf16 in the decode layouts (contiguous
+    [B, max_kv_len, Hkv, d], or pages [num_pages, 16, Hkv, d] with block_table
+    int32 [B, pages_per_seq]); seqlens int32 [B] cached tokens, the new ones
+    included. Returns o [B,Hq,Sq,d] bf16."""
+    torch = _torch()
+    _dev(q, kcache, vcache, seqlens, block_table, o)
+    _contig(q, kcache, vcache, seqlens, block_table, o)
+    if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
+        raise ValueError("prefill_cache takes bfloat16 q and caches")
+    if seqlens.dtype != torch.int32 or (block_table is not None and block_table.dtype != torch.int32):
+        raise ValueError("seqlens and block_table must be int32")
+    B, Hq, Sq, d = q.shape
+    Hkv = kcache.shape[2]
+    if kcache.shape != vcache.shape or kcache.shape[3] != d:
+        raise ValueError("kcache and vcache must match and end in [Hkv, d]")
+    if block_table is None:
+        if kcache.shape[0] != B:
+            raise ValueError("contiguous cache must be [B, max_kv_len, Hkv, d]")
+        mkl = kcache.shape[1] if max_kv_len is None else int(max_kv_len)
+        page = 0
+    else:
+        if kcache.shape[1] != 16 or block_table.shape[0] != B:
+            raise ValueError("paged cache must be [num_pages, 16, Hkv, d] with block_table [B, pages]")
+        mkl = 16 * block_table.shape[1] if max_kv_len is None else int(max_kv_len)
+        if (mkl + 15) // 16 != block_table.shape[1]:
+            raise ValueError("block_table must have ceil(max_kv_len/16) columns")
+        page = 16
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    check(lib().fa_prefill_cache(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens), _ptr(o), B,
+                                 Hq, Hkv, Sq, d, mkl, page, float(scale), int(bool(causal)), _stream_handle(q, stream)))
     return o
 
 

@@ -117,6 +117,26 @@ fa_status fa_prefill(const void* q, const void* k, const void* v, void* o, int B
   return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
 }
 
+fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                           const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int Sq, int d, int max_kv_len,
+                           int page_size, float scale, int causal, void* stream) {
+  if (!seqlens) return FA_ERR_NULL;
+  // the checks of fa_prefill with Skv = max_kv_len, without its causal bound
+  // Sq <= Skv (here a row with no visible key gives zeros)
+  fa_status st = check_prefill(q, kcache, vcache, o, B, Hq, Hkv, Sq, max_kv_len, d, scale, 0);
+  if (st != FA_OK) return st;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (block_table && page_size != 16) return FA_ERR_UNSUPPORTED;
+  if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
+  if (!block_table && (size_t)B * (size_t)max_kv_len > (size_t)INT32_MAX) return FA_ERR_SHAPE;
+  fa::PrefillParams p = make_prefill(q, kcache, vcache, o, B, Hq, Hkv, Sq, max_kv_len, scale, causal);
+  p.lens = seqlens;
+  p.bt = block_table;
+  p.max_len = max_kv_len;
+  p.pps = (max_kv_len + 15) / 16;
+  return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+}
+
 fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq,
                          int Skv, int d, float scale, int causal, void* stream) {
   fa_status st = check_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, scale, causal);

@@ -30,6 +30,11 @@ struct PrefillParams {
   int causal;  // bottom-right aligned
   int nT;      // query tiles of 128 rows
   int nP;      // work-groups per (b, h): pairs of query tiles
+  // KV-cache prefill (bf16 kernel only): lens != nullptr selects it. k, v are
+  // then the K / V caches in the decode layouts, Skv = clamp(lens[b], 0, max_len).
+  const int32_t* lens = nullptr;
+  const int32_t* bt = nullptr;  // block table [B, pps] or nullptr (contiguous cache)
+  int max_len = 0, pps = 0;
 };
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);

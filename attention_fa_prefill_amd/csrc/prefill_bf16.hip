@@ -109,7 +109,13 @@ __device__ __forceinline__ void wait_dma() {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
-template <int D>
+// CACHE: K and V come from a KV cache in the decode layouts (contiguous
+// [B, max_len, Hkv, D] or pages of 16 tokens [pages, 16, Hkv, D] through a
+// block table) with Skv = seqlens[b] per sequence: the chunked prefill of a
+// serving loop, whose Sq new queries are the last Sq of the Skv cached tokens
+// (bottom-right causal alignment). A query row with no visible key (causal,
+// Skv < Sq) gives zeros.
+template <int D, bool CACHE>
 __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   using C = Cfg<D>;
   // Two stages x {K, V}, each holding both groups' blocks, plus a staging area
@@ -143,14 +149,16 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     b = I / (p.nP * p.Hq);
   }
   const int g = (int)((long)h * p.Hkv / p.Hq);
-  const int Sq = p.Sq, Skv = p.Skv;
+  const int Sq = p.Sq;
+  const int Skv = CACHE ? min(max(p.lens[b], 0), p.max_len) : p.Skv;
   const int off = Skv - Sq;
   const bool causal = p.causal != 0;
   const float c = p.c;
 
   auto nblocks = [&](int t) __attribute__((always_inline)) {
     const int end = causal ? min(Skv, (t + 1) * kBM + off) : Skv;
-    return (end + kBN - 1) / kBN;
+    const int n = (end + kBN - 1) / kBN;
+    return CACHE ? max(0, n) : n;  // (CACHE: a causal tile above every key has none)
   };
   const int t0 = pidx, t1 = p.nT - 1 - pidx;
   const int n1 = nblocks(t1);
@@ -162,27 +170,52 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   auto kv_of = [&](int i) __attribute__((always_inline)) { return grp ? i : (i < nA0 ? i : jB + (i - nA0)); };
   auto tile_of = [&](int i) __attribute__((always_inline)) { return grp ? t1 : (i < nA0 ? t0 : t1); };
 
-  const __bf16* kbh = (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
-  const __bf16* vbh = (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* kbh = CACHE ? (const __bf16*)p.k : (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* vbh = CACHE ? (const __bf16*)p.v : (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
   const __bf16* qbh = (const __bf16*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
 
   // Per-lane byte offsets (inside a 64-key block) of this lane's direct-to-LDS
   // loads: LDS chunk P of the block holds logical chunk (P % CH) ^ swz(row) of
   // row P / CH.
+  // (CACHE: wave wg's loads of a block cover exactly its 16 rows 16 wg ..
+  // 16 wg + 15, one page, and rows are rowstride bytes apart.)
+  static_assert(64 * C::NI / C::CH == 16, "one page of rows per wave and block");
+  const uint32_t rowstride = CACHE ? (uint32_t)p.Hkv * D * 2u : (uint32_t)D * 2u;
   uint32_t koff[C::NI], voff[C::NI];
 #pragma unroll
   for (int ii = 0; ii < C::NI; ++ii) {
     const int P = 64 * (wg * C::NI + ii) + lane;
     const int row = P / C::CH, pc = P % C::CH;
-    koff[ii] = (uint32_t)(row * D + ((pc ^ swz_k<D>(row)) << 3)) * 2u;
-    voff[ii] = (uint32_t)(row * D + ((pc ^ swz_v<D>(row)) << 3)) * 2u;
+    const uint32_t rbase = (uint32_t)(CACHE ? (row & 15) : row) * rowstride;
+    koff[ii] = rbase + (uint32_t)((pc ^ swz_k<D>(row)) << 4);
+    voff[ii] = rbase + (uint32_t)((pc ^ swz_v<D>(row)) << 4);
   }
+  // CACHE: buffer resource over this wave's page of block j of the K (or V)
+  // cache; its record count ends after the last key that exists, so rows past
+  // Skv read as zero, and a page past the sequence is neither looked up in the
+  // block table nor read.
+  // The cache row of the page comes from page_row, looked up ahead of the
+  // loads (a scalar load waited for next to the loads would stall the MFMA
+  // stream once per load).
+  auto page_row = [&](int j, bool valid) __attribute__((always_inline)) {
+    const int r0 = j * kBN + 16 * wg;
+    if (!CACHE || !valid || r0 >= Skv) return (long)-1;
+    return p.bt ? (long)p.bt[(size_t)b * p.pps + r0 / 16] * 16 : (long)b * p.max_len + r0;
+  };
+  auto page_rsrc = [&](const __bf16* cache, int j, long prow) __attribute__((always_inline)) {
+    const int r0 = j * kBN + 16 * wg;
+    const int nvalid = prow >= 0 ? max(0, min(16, Skv - r0)) : 0;
+    const char* base = (const char*)cache;
+    if (nvalid > 0) base += ((size_t)prow * p.Hkv + g) * (size_t)(D * 2);
+    const int nrec = nvalid > 0 ? (nvalid - 1) * (int)rowstride + D * 2 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrec, kRsrcWord3);
+  };
   // One K or V block -> this group's slot of an LDS stage. The buffer resource
   // covers only the keys that exist, so rows past Skv read as zero.
-  auto dma_one = [&](const __bf16* src_bh, __bf16* stage, const uint32_t* offs, int j, bool valid, int ii) __attribute__((always_inline)) {
+  auto dma_one = [&](const __bf16* src_bh, __bf16* stage, const uint32_t* offs, int j, bool valid, int ii, long prow) __attribute__((always_inline)) {
     const int kv0 = j * kBN;
     const int rows = valid ? min(kBN, Skv - kv0) : 0;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+    const __amdgpu_buffer_rsrc_t rs = CACHE ? page_rsrc(src_bh, j, prow) : __builtin_amdgcn_make_buffer_rsrc(
         (void*)(src_bh + (size_t)(valid ? kv0 : 0) * D), (short)0, rows * D * 2, kRsrcWord3);
     __bf16* dst0 = stage + grp * C::ELEMS;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst0 + 64 * (wg * C::NI + ii) * 8), 16, (int)offs[ii], 0,
@@ -191,7 +224,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   auto dma = [&](const __bf16* src_bh, __bf16* stage, const uint32_t* offs, int j) __attribute__((always_inline)) {
     const int kv0 = j * kBN;
     const int rows = min(kBN, Skv - kv0);
-    const __amdgpu_buffer_rsrc_t rs =
+    const __amdgpu_buffer_rsrc_t rs = CACHE ? page_rsrc(src_bh, j, page_row(j, true)) :
         __builtin_amdgcn_make_buffer_rsrc((void*)(src_bh + (size_t)kv0 * D), (short)0, rows * D * 2, kRsrcWord3);
     __bf16* dst0 = stage + grp * C::ELEMS;
 #pragma unroll
@@ -254,7 +287,8 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
 
   auto store_tile = [&](int t) __attribute__((always_inline)) {
     const float lt = pair_sum(l_run);
-    const float inv = 1.0f / lt;
+    // (CACHE: a row with no visible key has l = 0 and gives zeros)
+    const float inv = CACHE ? (lt > 0.f ? 1.0f / lt : 0.f) : 1.0f / lt;
     const int row = t * kBM + wg * 32 + ln;
     if (row < Sq) {
       __bf16* dst = (__bf16*)p.o + (((size_t)b * p.Hq + h) * Sq + row) * D;
@@ -322,6 +356,8 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
       const int j = i - kPV;
       return kread(kbase, (j & 1) ? kr1 : kr0, (j & 1) ? sw1 : sw0, j >> 1);
     };
+    // (CACHE: this wave's page rows of K(k+1) and V(k), looked up first)
+    const long prk = page_row(kv_of(k + 1), k + 1 < cnt), prv = page_row(kv_of(k), k < cnt);
     bf16x8 buf[kPF];
 #pragma unroll
     for (int i = 0; i < kPF; ++i) buf[i] = opnd(i);
@@ -334,9 +370,9 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
         // one direct-to-LDS load between MFMAs: K of block k+1, then V of block k
         const int n = (i - kPV) >> 1;
         if (n < C::NI)
-          dma_one(kbh, sKn, koff, kv_of(k + 1), k + 1 < cnt, n);
+          dma_one(kbh, sKn, koff, kv_of(k + 1), k + 1 < cnt, n, prk);
         else
-          dma_one(vbh, sVc, voff, kv_of(k), k < cnt, n - C::NI);
+          dma_one(vbh, sVc, voff, kv_of(k), k < cnt, n - C::NI, prv);
       }
       if (i < kPV) {
         const int sub = i / (2 * C::DB), ss = (i / C::DB) & 1, db = i % C::DB;
@@ -471,6 +507,11 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
     for (int i = 0; i < C::ELEMS / 8 / 4 / 64; ++i) z[i * 64 + lane] = make_uint4(0, 0, 0, 0);
   }
+  if (CACHE && grp == 0 && nA0 == 0 && t0 != t1) {
+    // tile t0 sees no key at all (causal, Skv < Sq): its rows are zeros
+    reset_state();
+    store_tile(t0);
+  }
   if (cnt > 0) {
     dma(kbh, sK0, koff, kv_of(0));
     cur_tile = tile_of(0);
@@ -554,10 +595,15 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
   dim3 grid(p.nP * p.Hq * p.B), block(512);
-  if (d == 128)
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, stream, p);
+  const bool cache = p.lens != nullptr;
+  if (d == 128 && !cache)
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, p);
+  else if (d == 64 && !cache)
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, p);
+  else if (d == 128)
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

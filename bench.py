@@ -286,7 +286,7 @@ def main():
     traffic = traffic_for("prefill_bf16_kernel<128>@prefill_gqa_b1h32x8s2048d128", PREFILL_KERNEL_SRC)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "prefill_bf16_kernel<128>", "mean_launch_us": round(mean_launch_ms * 1e3, 2),
+                "kernel": "prefill_bf16_kernel<128, false>", "mean_launch_us": round(mean_launch_ms * 1e3, 2),
                 "algorithmic_flop_per_launch": flops,
                 "algorithmic_bytes_per_launch": prefill_bytes(B, Hq, Hkv, Sq, Skv, d)}
 
@@ -316,6 +316,40 @@ def main():
             "traffic": traffic_for("decode_split_kernel<128, fp8>@decode_long_b1h16x2kv256kd128_fp8", DECODE_KERNEL_SRC),
             "workload": "decode_long_b1h16x2kv256kd128_fp8",
             "note": "FP8 E4M3 cache (1 byte per element); split + merge kernels per call, caches evicted before each call"}
+
+        # chunked prefill over a paged KV cache (fa_prefill_cache): back-to-back
+        # calls with the cache resident, the same timing as the headline
+        pc = workloads.prefill_cache_chunk512()
+        pq, pk, pv = bf16(pc.q), bf16(pc.kcache), bf16(pc.vcache)
+        plens, pbt = i32(pc.seqlens), i32(pc.block_table)
+        po = torch.empty_like(pq)
+        pargs = (ctypes.c_void_p(pq.data_ptr()), ctypes.c_void_p(pk.data_ptr()), ctypes.c_void_p(pv.data_ptr()),
+                 ctypes.c_void_p(pbt.data_ptr()), ctypes.c_void_p(plens.data_ptr()), ctypes.c_void_p(po.data_ptr()),
+                 pc.B, pc.Hq, pc.Hkv, pc.Sq, pc.d, pc.max_kv_len, 16, pc.scale, 1, ctypes_stream)
+
+        def pcall():
+            st = L.fa_prefill_cache(*pargs)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+        for _ in range(200):
+            pcall()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(100):
+            pcall()
+        ev1.record(stream)
+        ev1.synchronize()
+        pc_us = ev0.elapsed_time(ev1) * 1e3 / 100
+        pc_flop = sum(prefill_flops(1, pc.Hq, pc.Sq, int(L_), pc.d, True) for L_ in pc.seqlens)
+        result["prefill_cache"] = {
+            "workload": pc.name, "us_per_call_mean": round(pc_us, 2),
+            "TFLOP_per_s": round(pc_flop / (pc_us * 1e-6) / 1e12, 1),
+            "frac_of_bf16_peak": round(pc_flop / (pc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop_per_call": pc_flop, "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "Sq": pc.Sq, "d": pc.d,
+            "cached_lengths": [int(x) for x in pc.seqlens], "paged": True, "causal": True,
+            "note": "chunk of Sq new queries per sequence over its paged cache (chunk included); 100 back-to-back calls"}
+        del pq, pk, pv, plens, pbt, po
 
         # fp32 single-head causal prefill at B=1 (launch-latency bound)
         c1 = workloads.prefill_f32_small()

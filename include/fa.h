@@ -105,6 +105,36 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
                          float scale, int causal, void* stream);
 
 /*
+ * fa_prefill_cache - fa_prefill with K and V read from a KV cache: the chunked
+ * prefill of a serving loop, where each sequence's Sq new tokens have been
+ * appended to its cache and attend to all of its cached tokens. Context and
+ * generation phases with a KV cache are the FasterTransformer walkthrough's
+ * sections 3.1 and 3.2; the cache layouts, page size and block table are
+ * those of fa_decode (the paged sketch of the real-time inference page).
+ *
+ *   q, o        : bf16 [B, Hq, Sq, d], the new queries of each sequence.
+ *   kcache, vcache, block_table, page_size, max_kv_len : as for fa_decode
+ *                 (contiguous bf16 [B, max_kv_len, Hkv, d], or pages of 16
+ *                 tokens through the block table).
+ *   seqlens     : int32 [B] device array: cached tokens of each sequence,
+ *                 the Sq new ones included, clamped to [0, max_kv_len].
+ *   causal      : 1 -> query row i of sequence b sees cached tokens
+ *                 j <= i + seqlens[b] - Sq (the new tokens are the last Sq);
+ *                 a row that sees no token (seqlens[b] < Sq) gives zeros.
+ *                 0 -> every row sees all seqlens[b] tokens (zeros if none).
+ *   scale, d, stream, errors : as for fa_prefill (d = 64 or 128), plus
+ *                 FA_ERR_NULL for a NULL seqlens and FA_ERR_UNSUPPORTED for a
+ *                 page size other than 16.
+ * With a contiguous cache holding exactly the K and V of fa_prefill
+ * (max_kv_len = Skv, seqlens all Skv) the result equals fa_prefill's bit for
+ * bit: the same kernel does the same arithmetic in the same order.
+ */
+fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* block_table, const int32_t* seqlens, void* o,
+                           int B, int Hq, int Hkv, int Sq, int d, int max_kv_len,
+                           int page_size, float scale, int causal, void* stream);
+
+/*
  * fa_decode_split_tokens - the KV tokens each split work-group of fa_decode
  * covers (n_split = ceil(max_kv_len / result) splits per sequence; this sizes
  * the workspace).

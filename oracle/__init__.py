@@ -135,6 +135,47 @@ def decode(q, kcache, vcache, seqlens, scale: float, block_table=None, page_size
     return o, lse
 
 
+def prefill_cache(q, kcache, vcache, seqlens, scale: float, causal: bool, block_table=None, page_size: int = 16,
+                  max_kv_len=None, lib: str | None = None):
+    """Chunked prefill over a KV cache, in fp64: sequence b's keys are its
+    first L_b = clamp(seqlens[b], 0, max_kv_len) cached tokens, gathered from
+    the cache (contiguous [B, max_kv_len, Hkv, d], or pages [P, page, Hkv, d]
+    through block_table [B, pages]), and its Sq queries q[b] are the last Sq
+    of them: with causal, row i sees tokens j <= i + L_b - Sq. A row that sees
+    no token is zero (softmax over an empty set taken as an empty sum).
+    Returns o [B, Hq, Sq, d]."""
+    q, kc, vc = _f64(q), _f64(kcache), _f64(vcache)
+    B, Hq, Sq, d = q.shape
+    Hkv = kc.shape[2]
+    lens = np.asarray(seqlens, dtype=np.int64)
+    if block_table is None:
+        mkl = kc.shape[1] if max_kv_len is None else int(max_kv_len)
+    else:
+        bt = np.asarray(block_table, dtype=np.int64)
+        mkl = bt.shape[1] * int(page_size) if max_kv_len is None else int(max_kv_len)
+    o = np.zeros((B, Hq, Sq, d), dtype=np.float64)
+    for b in range(B):
+        L = int(min(max(lens[b], 0), mkl))
+        if L == 0:
+            continue
+        t = np.arange(L)
+        if block_table is None:
+            kb, vb = kc[b, :L], vc[b, :L]                      # [L, Hkv, d]
+        else:
+            rows = bt[b, t // page_size], t % page_size
+            kb, vb = kc[rows], vc[rows]
+        kb = np.ascontiguousarray(kb.transpose(1, 0, 2))[None]  # [1, Hkv, L, d]
+        vb = np.ascontiguousarray(vb.transpose(1, 0, 2))[None]
+        if causal and L < Sq:
+            # rows i < Sq - L see nothing; the rest are the last L rows over L keys
+            ob, _ = attention(q[b:b + 1, :, Sq - L:], kb, vb, scale, True, lib=lib)
+            o[b, :, Sq - L:] = ob[0]
+        else:
+            ob, _ = attention(q[b:b + 1], kb, vb, scale, causal, lib=lib)
+            o[b] = ob[0]
+    return o
+
+
 def e4m3_to_f64(codes) -> np.ndarray:
     """OCP 8-bit floating point E4M3 (the "FN" variant: no infinities) to
     fp64, from the definition of the format: bit 7 sign, bits 6..3 exponent

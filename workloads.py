@@ -240,6 +240,58 @@ def paged_from_contiguous(case: DecodeCase, seed: int = 99) -> DecodeCase:
                       case.seqlens.copy(), case.q, kp, vp, bt, case.fp8, case.k_scale, case.v_scale)
 
 
+# --------------------------------------------------------------------------- chunked prefill over a KV cache
+
+
+@dataclass
+class PrefillCacheCase:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    d: int
+    max_kv_len: int
+    scale: float
+    causal: bool
+    seqlens: np.ndarray  # int32 [B]: cached tokens, the Sq new ones included
+    q: np.ndarray = field(repr=False)  # bf16 bits [B, Hq, Sq, d]
+    kcache: np.ndarray = field(repr=False)  # decode layouts (contiguous or page pool)
+    vcache: np.ndarray = field(repr=False)
+    block_table: np.ndarray | None = field(default=None, repr=False)
+
+    @property
+    def paged(self) -> bool:
+        return self.block_table is not None
+
+
+def prefill_cache_case(B, Hq, Hkv, Sq, d, seqlens, max_kv_len, paged=True, causal=True, seed=13, name=None,
+                       poison=False) -> PrefillCacheCase:
+    """Sq new queries per sequence (N(0,1), bf16) over a cache built like the
+    decode caches (same generators, same seed): contiguous [B, max_kv_len,
+    Hkv, d] or a shuffled pool of 16-token pages. With poison, slots past each
+    length and the slack pages hold NaN."""
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    if paged:
+        dc = decode_paged(B, Hq, Hkv, d, seqlens, max_kv_len, seed=seed, poison=poison)
+    else:
+        dc = decode_contiguous(B, Hq, Hkv, d, max_kv_len, seqlens=seqlens, seed=seed, poison=poison)
+    q = normal_bf16(seed, 8, (B, Hq, Sq, d))
+    if name is None:
+        name = f"prefill_cache_b{B}h{Hq}x{Hkv}sq{Sq}kv{max_kv_len}d{d}{'_paged' if paged else ''}"
+    return PrefillCacheCase(name, B, Hq, Hkv, Sq, d, int(max_kv_len), 1.0 / math.sqrt(d), bool(causal), seqlens, q,
+                            dc.kcache, dc.vcache, dc.block_table)
+
+
+def prefill_cache_chunk512() -> PrefillCacheCase:
+    """Chunked prefill: B=4, Hq=32, Hkv=8, d=128, a chunk of 512 new tokens per
+    sequence, cached lengths (chunk included) U{2048..16384}, page 16, shuffled
+    pool, causal."""
+    lens = paged_lengths(1006, 4, 2048, 16384)
+    return prefill_cache_case(4, 32, 8, 512, 128, lens, 16384, paged=True, causal=True, seed=1006,
+                              name="prefill_cache_b4h32x8sq512kv2k16kd128")
+
+
 # --------------------------------------------------------------------------- fp8 KV cache
 
 FP8_NAN = 0x7F  # an OCP FP8 E4M3 NaN code
