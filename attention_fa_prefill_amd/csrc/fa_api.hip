@@ -129,6 +129,10 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
   if (block_table && page_size != 16) return FA_ERR_UNSUPPORTED;
   if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
   if (!block_table && (size_t)B * (size_t)max_kv_len > (size_t)INT32_MAX) return FA_ERR_SHAPE;
+  // one work-group per (query tile, head, sequence), padded to whole rounds of
+  // (sequence, kv head) groups on the 8 XCDs
+  const long tiles = ((long)Sq + 127) / 128;
+  if (8 * (((long)B * Hkv + 7) / 8) * (Hq / Hkv) * tiles > (long)INT32_MAX) return FA_ERR_SHAPE;
   fa::PrefillParams p = make_prefill(q, kcache, vcache, o, B, Hq, Hkv, Sq, max_kv_len, scale, causal);
   p.lens = seqlens;
   p.bt = block_table;

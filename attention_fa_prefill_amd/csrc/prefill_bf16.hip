@@ -54,7 +54,8 @@ constexpr int kBM = 128;     // query rows per wave group
 constexpr int kBN = 64;      // keys per KV block
 constexpr float kTau = 8.0f; // lazy rescale threshold (log2 units)
 constexpr float kRedo = 65536.0f;  // partial row sum above which a block is redone with its maximum
-constexpr int kXcds = 8;     // MI355X: 8 accelerator complex dies, one L2 each
+constexpr int kXcds = 8;
+constexpr int kRankMaxB = 512;  // sequences ordered by length in every work-group up to this batch     // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
 template <int D>
@@ -138,7 +139,42 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   // XCD-aware work order: work item I (pair fastest, then query head, then
   // batch) goes to the work-group that puts contiguous item ranges on one XCD.
   int pidx, h, b;
-  {
+  if constexpr (CACHE) {
+    // One query tile per work-group (both groups split its keys, as for the
+    // middle tile of an odd tile count): with a cache the tiles of a sequence
+    // cost about the same, and the cost is its cached length, which differs
+    // between sequences. The (sequence, kv head) groups are ordered by
+    // descending cached length and dealt round-robin to the 8 XCDs, whole, so
+    // each XCD gets an equal mix of long and short sequences, runs its longest
+    // work first, and keeps a kv head's K/V in one L2.
+    const int G = p.Hq / p.Hkv;
+    const int per_group = G * p.nT;
+    const int xcd = (int)blockIdx.x % kXcds, idx = (int)blockIdx.x / kXcds;
+    const int k = xcd + kXcds * (idx / per_group);
+    if (k >= p.B * p.Hkv) return;  // past this XCD's groups (uniform)
+    const int within = idx % per_group;
+    const int r = k / p.Hkv;
+    h = (k % p.Hkv) * G + within / p.nT;
+    pidx = within % p.nT;
+    // the sequence of length rank r (longest first, ties by index); beyond
+    // kRankMaxB sequences, index order
+    b = r;
+    if (p.B <= kRankMaxB) {
+      int* rank_slot = (int*)sQ;  // sQ is not in use yet
+      if (tid < p.B) {
+        const int lt = min(max(p.lens[tid], 0), p.max_len);
+        int rank = 0;
+        for (int u = 0; u < p.B; ++u) {
+          const int lu = min(max(p.lens[u], 0), p.max_len);
+          rank += (lu > lt || (lu == lt && u < tid)) ? 1 : 0;
+        }
+        if (rank == r) *rank_slot = tid;
+      }
+      __syncthreads();
+      b = __builtin_amdgcn_readfirstlane(*rank_slot);
+      __syncthreads();  // every wave has read the slot before sQ is reused
+    }
+  } else {
     const int W = p.nP * p.Hq * p.B;
     const int L = blockIdx.x;
     const int xcd = L % kXcds, idx = L / kXcds;
@@ -160,7 +196,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     const int n = (end + kBN - 1) / kBN;
     return CACHE ? max(0, n) : n;  // (CACHE: a causal tile above every key has none)
   };
-  const int t0 = pidx, t1 = p.nT - 1 - pidx;
+  const int t0 = pidx, t1 = CACHE ? pidx : p.nT - 1 - pidx;
   const int n1 = nblocks(t1);
   const int nA0 = (t0 == t1) ? 0 : nblocks(t0);
   const int jB = min(n1, (nA0 + n1 + 1) / 2);  // group B: t1 blocks [0, jB)
@@ -594,8 +630,12 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
 }  // namespace
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream) {
-  dim3 grid(p.nP * p.Hq * p.B), block(512);
   const bool cache = p.lens != nullptr;
+  // cache: one work-group per (tile, head, sequence), padded to whole rounds of
+  // (sequence, kv head) groups per XCD (the padding work-groups exit at once)
+  const long groups = (long)p.B * p.Hkv, per_group = (long)(p.Hq / p.Hkv) * p.nT;
+  dim3 grid(cache ? (unsigned)(kXcds * ((groups + kXcds - 1) / kXcds) * per_group) : (unsigned)(p.nP * p.Hq * p.B));
+  dim3 block(512);
   if (d == 128 && !cache)
     hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, p);
   else if (d == 64 && !cache)

@@ -125,9 +125,11 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
  *   scale, d, stream, errors : as for fa_prefill (d = 64 or 128), plus
  *                 FA_ERR_NULL for a NULL seqlens and FA_ERR_UNSUPPORTED for a
  *                 page size other than 16.
- * With a contiguous cache holding exactly the K and V of fa_prefill
- * (max_kv_len = Skv, seqlens all Skv) the result equals fa_prefill's bit for
- * bit: the same kernel does the same arithmetic in the same order.
+ * The same kernel as fa_prefill computes it, with one query tile per
+ * work-group (the sequences' tiles ordered by cached length, longest first),
+ * so with a cache holding exactly fa_prefill's K and V the two agree to
+ * rounding. For the same seqlens the paged and contiguous caches give
+ * bitwise equal results.
  */
 fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache,
                            const int32_t* block_table, const int32_t* seqlens, void* o,

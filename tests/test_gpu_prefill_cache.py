@@ -61,17 +61,24 @@ def test_shapes(shape):
             assert np.all(got[b] == 0.0)
 
 
-def test_full_cache_equals_prefill_bitwise():
+def test_full_cache_matches_prefill():
     """A contiguous cache holding exactly prefill's K and V (every length =
-    max_kv_len = Skv): fa_prefill_cache gives fa_prefill's bits."""
+    max_kv_len = Skv): fa_prefill_cache agrees with fa_prefill. The two split
+    a tile's keys differently between the halves of a work-group (one tile
+    per work-group here, pairs of tiles there), so the agreement is to
+    rounding, not bitwise; both are also held to the oracle."""
     torch = torch_gpu()
     case = workloads.prefill_cache_case(2, 8, 2, 700, 128, [1100, 1100], 1100, paged=False, causal=True, seed=71)
-    o_cache = run(case)
+    o_cache = host_f64(run(case))
     k = dev_bf16(case.kcache).permute(0, 2, 1, 3).contiguous()  # [B, Hkv, Skv, d]
     v = dev_bf16(case.vcache).permute(0, 2, 1, 3).contiguous()
-    o_plain = fa.prefill(dev_bf16(case.q), k, v, causal=True, scale=case.scale)
+    o_plain = host_f64(fa.prefill(dev_bf16(case.q), k, v, causal=True, scale=case.scale))
     torch.cuda.synchronize()
-    assert np.array_equal(host_bits(o_cache), host_bits(o_plain))
+    ref = oracle_out(case)
+    assert_bf16_close(o_cache, ref, "cache")
+    assert_bf16_close(o_plain, ref, "plain")
+    diff = np.abs(o_cache - o_plain)
+    assert diff.max() <= 1e-2 and diff.mean() <= 1e-4
 
 
 def test_paged_equals_contiguous_bitwise():
