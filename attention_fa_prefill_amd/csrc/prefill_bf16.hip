@@ -154,8 +154,9 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     if (k >= p.B * p.Hkv) return;  // past this XCD's groups (uniform)
     const int within = idx % per_group;
     const int r = k / p.Hkv;
-    h = (k % p.Hkv) * G + within / p.nT;
-    pidx = within % p.nT;
+    // inside a group, tiles by descending (causal) cost, then heads
+    h = (k % p.Hkv) * G + within % G;
+    pidx = p.nT - 1 - within / G;
     // the sequence of length rank r (longest first, ties by index); beyond
     // kRankMaxB sequences, index order
     b = r;
