@@ -102,3 +102,15 @@ def test_poisoned_slots_do_not_leak():
     o_dirty = run(dirty)
     assert np.all(np.isfinite(host_f64(o_dirty)))
     assert np.array_equal(host_bits(o_dirty), host_bits(run(clean)))
+
+
+@pytest.mark.parametrize("B", [37, 600])
+def test_many_sequences_mixed_lengths(B):
+    """Many short sequences with mixed lengths (zeros included): up to 512
+    sequences the work-groups order them by length; beyond, by index. Either
+    way every (tile, head, sequence) is computed once."""
+    lens = np.random.default_rng(B).integers(0, 200, size=B).astype(np.int32)
+    case = workloads.prefill_cache_case(B, 2, 1, 40, 64, lens, 208, paged=True, causal=True, seed=B)
+    got = host_f64(run(case))
+    assert_bf16_close(got, oracle_out(case), f"B={B}")
+    assert np.all(got[lens == 0] == 0.0)
