@@ -34,6 +34,11 @@
 // Paged and contiguous caches run the same instructions in the same order and
 // differ only in the row address, so their results are bitwise equal.
 //
+// An FP8 E4M3 cache (one byte per element, one scale per tensor) runs the same
+// kernel: K is widened to bf16 in registers, V goes to LDS as bytes and comes
+// back through the 8-bit transpose read, both exactly; the K scale is folded
+// into the softmax factor and the V scale into each split's output.
+//
 // Merge kernel: per row, M = max lse_s, w_s = exp(lse_s - M),
 // o = sum_s w_s o_s / sum_s w_s, lse = M + log(sum_s w_s); empty splits skipped.
 #include <type_traits>

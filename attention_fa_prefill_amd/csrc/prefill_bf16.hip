@@ -20,6 +20,10 @@
 //     HBM into one L2 and reused there.
 //   - K/V blocks of 64 keys go HBM/L2 -> LDS with 16-byte direct-to-LDS buffer
 //     loads, double-buffered per group, issued two slots ahead of their use.
+//   - The KV-cache variant (chunked prefill) reads K/V pages of 16 tokens from
+//     a contiguous or paged cache, one buffer resource per page, and gives each
+//     work-group one tile; the (sequence, kv head) groups are ordered by
+//     descending cached length (see the kernel's template comment).
 //
 // Per wave and per 64-key block (two 32-key sub-tiles):
 //   S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T held
