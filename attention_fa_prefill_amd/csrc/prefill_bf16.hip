@@ -373,7 +373,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
 
   // MFMA slot k: PV of block k-1, tile switch if block k starts a new tile,
   // then S of block k. (sKc: K stage of block k; sVp: V stage of block k-1;
-  // sKn, sVc: stages that receive K of block k+1 and V of block k.)
+  // sKn: stage that receives K of block k+1.)
   // It runs as one stream of 32 MFMAs - 16 of PV, then 16 of S - whose LDS
   // operands are read kPF MFMAs ahead, so the matrix core does not wait on LDS
   // latency. When no PV is pending its probabilities are zero (the V stage
@@ -382,7 +382,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   constexpr int kPV = 4 * C::DB;  // PV MFMAs: (sub, s, db)
   constexpr int kS = 2 * C::KS;   // S MFMAs: (ks, sub)
   constexpr int kPF = 4;          // operand prefetch distance (MFMAs)
-  auto mslot = [&](int k, const __bf16* sKc, const __bf16* sVp, __bf16* sKn, __bf16* sVc) __attribute__((always_inline)) {
+  auto mslot = [&](int k, const __bf16* sKc, const __bf16* sVp, __bf16* sKn) __attribute__((always_inline)) {
     const char* vbase = (const char*)(sVp + grp * C::ELEMS);
     const char* kbase = (const char*)(sKc + grp * C::ELEMS);
     if (!p_vis) {
@@ -397,8 +397,8 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
       const int j = i - kPV;
       return kread(kbase, (j & 1) ? kr1 : kr0, (j & 1) ? sw1 : sw0, j >> 1);
     };
-    // (CACHE: this wave's page rows of K(k+1) and V(k), looked up first)
-    const long prk = page_row(kv_of(k + 1), k + 1 < cnt), prv = page_row(kv_of(k), k < cnt);
+    // (CACHE: this wave's page row of K(k+1), looked up first)
+    const long prk = page_row(kv_of(k + 1), k + 1 < cnt);
     bf16x8 buf[kPF];
 #pragma unroll
     for (int i = 0; i < kPF; ++i) buf[i] = opnd(i);
@@ -407,13 +407,10 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     for (int i = 0; i < kPV + kS; ++i) {
       const bf16x8 a = buf[i % kPF];
       if (i + kPF < kPV + kS) buf[i % kPF] = opnd(i + kPF);
-      if (i >= kPV && i < kPV + 4 * C::NI && ((i - kPV) & 1) == 0) {
-        // one direct-to-LDS load between MFMAs: K of block k+1, then V of block k
+      if (i >= kPV && i < kPV + 2 * C::NI && ((i - kPV) & 1) == 0) {
+        // one direct-to-LDS load between every other MFMA: K of block k+1
         const int n = (i - kPV) >> 1;
-        if (n < C::NI)
-          dma_one(kbh, sKn, koff, kv_of(k + 1), k + 1 < cnt, n, prk);
-        else
-          dma_one(vbh, sVc, voff, kv_of(k), k < cnt, n - C::NI, prv);
+        dma_one(kbh, sKn, koff, kv_of(k + 1), k + 1 < cnt, n, prk);
       }
       if (i < kPV) {
         const int sub = i / (2 * C::DB), ss = (i / C::DB) & 1, db = i % C::DB;
@@ -463,7 +460,16 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   // when a row's partial sum shows that the block rose far above it
   // (> 2^16), is the block's maximum taken, the reference raised (lazily, by
   // more than kTau) with O and l rescaled, and the block redone.
-  auto vslot = [&]() __attribute__((always_inline)) {
+  // The slot first issues the loads of V of block k into sVc (free since the
+  // PV of block k-2), so the MFMA slot carries only the K loads: the direct-
+  // to-LDS issue (address and M0 set-up, and for the cache variant the page
+  // lookup) then overlaps the exponentials instead of delaying the MFMAs.
+  auto vslot = [&](int k, __bf16* sVc) __attribute__((always_inline)) {
+    {
+      const long prv = page_row(kv_of(k), k < cnt);
+#pragma unroll
+      for (int n = 0; n < C::NI; ++n) dma_one(vbh, sVc, voff, kv_of(k), k < cnt, n, prv);
+    }
     if (!s_vis) return;
     const int kv0 = s_kv0, q0 = s_q0;
     const bool full = kv0 + kBN <= Skv && (!causal || kv0 + kBN - 1 <= q0 + off);
@@ -578,17 +584,17 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     wait_dma();
     lds_barrier();
     __builtin_amdgcn_s_setprio(1);
-    mslot(k, sK0, sV1, sK1, sV0);
+    mslot(k, sK0, sV1, sK1);
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
-    if (k < cnt) vslot();
+    if (k < cnt) vslot(k, sV0);
     wait_dma();
     lds_barrier();
     __builtin_amdgcn_s_setprio(1);
-    if (k + 1 <= cnt) mslot(k + 1, sK1, sV0, sK0, sV1);
+    if (k + 1 <= cnt) mslot(k + 1, sK1, sV0, sK0);
     __builtin_amdgcn_s_setprio(0);
     lds_barrier();
-    if (k + 1 < cnt) vslot();
+    if (k + 1 < cnt) vslot(k + 1, sV1);
     nbar += 4;
   }
   {
