@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip"]
+SOURCES = ["fa_api.hip", "prefill_bf16.hip", "prefill_hd.hip", "prefill_f32.hip", "decode.hip"]
 CEILING_LIB = os.path.join(HERE, "libfa_ceiling.so")
 CEILING_SOURCES = ["ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

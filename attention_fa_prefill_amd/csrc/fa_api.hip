@@ -32,12 +32,13 @@ fa_status check_prefill(const void* q, const void* k, const void* v, void* o, in
   if (B > kMaxGridYZ || Hq > kMaxGridYZ) return FA_ERR_SHAPE;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (causal && Sq > Skv) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
-  // the bf16 kernel runs one work-group per (pair of 128-row query tiles, head, batch)
-  const long pairs = ((long)Sq + 255) / 256;
-  if (pairs * Hq * B > (long)INT32_MAX) return FA_ERR_SHAPE;
+  // the bf16 kernels run one work-group per (pair of 128-row query tiles, or
+  // one tile for the other head dims, head, batch)
+  const long tiles = ((long)Sq + 127) / 128;
+  if (tiles * Hq * B > (long)INT32_MAX) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -114,7 +115,8 @@ fa_status fa_prefill(const void* q, const void* k, const void* v, void* o, int B
   fa_status st = check_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, scale, causal);
   if (st != FA_OK) return st;
   fa::PrefillParams p = make_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, scale, causal);
-  return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+  if (d == 64 || d == 128) return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+  return from_hip(fa::launch_prefill_hd(p, d, (hipStream_t)stream));
 }
 
 fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
@@ -125,6 +127,7 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
   // Sq <= Skv (here a row with no visible key gives zeros)
   fa_status st = check_prefill(q, kcache, vcache, o, B, Hq, Hkv, Sq, max_kv_len, d, scale, 0);
   if (st != FA_OK) return st;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (block_table && page_size != 16) return FA_ERR_UNSUPPORTED;
   if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;

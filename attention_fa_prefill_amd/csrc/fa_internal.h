@@ -39,6 +39,7 @@ struct PrefillParams {
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream);
+hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream);
 
 // ---------------------------------------------------------------- decode
 struct DecodeParams {

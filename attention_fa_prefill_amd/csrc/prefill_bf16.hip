@@ -46,9 +46,9 @@
 // wave issues MFMA while the other issues the softmax. The barriers only order
 // LDS (no wait for outstanding HBM loads): a group waits for its own
 // direct-to-LDS loads right before the barrier that opens its next MFMA slot.
-// The loads of a block are issued one at a time between the S MFMAs of the
-// slot before (K of block k+1 and V of block k during M(k)), and the wave in
-// its MFMA slot runs at raised issue priority (s_setprio 1).
+// The K loads of block k+1 are issued one at a time between the MFMAs of
+// M(k), the V loads of block k at the start of V(k); the wave in its MFMA
+// slot runs at raised issue priority (s_setprio 1).
 #include "fa_internal.h"
 
 namespace fa {

@@ -11,10 +11,11 @@
 //   - a work-group (4 waves) owns 4 query rows; each wave takes every 4th block
 //     of 8 keys, so the keys of a row are split four ways;
 //   - inside a wave, 16 lanes share a row, each holding d/16 consecutive dims
-//     of q and of its accumulator; a score is a 4-FMA (or 8-FMA) partial dot
-//     product and a 16-lane sum over DPP (quad permutes, then half-row and
-//     row mirrors);
-//   - K and V rows are read straight from global memory as float4s (the four
+//     of q and of its accumulator (d = 32, 64, 96, 128 or 256); a score is a
+//     d/16-FMA partial dot product and a 16-lane sum over DPP (quad permutes,
+//     then half-row and row mirrors);
+//   - K and V rows are read straight from global memory as float4s, or
+//     float2s where d/16 is not a multiple of 4 (the four
 //     rows of a wave read the same addresses, which the cache merges), so no
 //     LDS staging and no barrier sits on the path;
 //   - probabilities use exp2 of scores pre-multiplied by scale*log2(e);
@@ -35,6 +36,35 @@ __device__ __forceinline__ float row16_sum(float x) {
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, true));  // row_half_mirror
   x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, true));  // row_mirror
   return x;
+}
+
+// DP consecutive floats: float4 accesses when DP is a multiple of 4, else
+// float2 (d = 32, 96); the row offsets keep them 16- or 8-byte aligned.
+template <int DP>
+__device__ __forceinline__ void load_dp(const float* src, float* dst) {
+  if constexpr (DP % 4 == 0) {
+#pragma unroll
+    for (int e = 0; e < DP; e += 4) {
+      const float4 x = *(const float4*)(src + e);
+      dst[e] = x.x; dst[e + 1] = x.y; dst[e + 2] = x.z; dst[e + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < DP; e += 2) {
+      const float2 x = *(const float2*)(src + e);
+      dst[e] = x.x; dst[e + 1] = x.y;
+    }
+  }
+}
+template <int DP>
+__device__ __forceinline__ void store_dp(float* dst, const float* src, float f) {
+  if constexpr (DP % 4 == 0) {
+#pragma unroll
+    for (int e = 0; e < DP; e += 4) *(float4*)(dst + e) = make_float4(src[e] * f, src[e + 1] * f, src[e + 2] * f, src[e + 3] * f);
+  } else {
+#pragma unroll
+    for (int e = 0; e < DP; e += 2) *(float2*)(dst + e) = make_float2(src[e] * f, src[e + 1] * f);
+  }
 }
 
 template <int D>
@@ -58,11 +88,10 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillParams p) {
   float q[DP], acc[DP];
   {
     const float* qrow = (const float*)p.q + (((size_t)b * p.Hq + h) * Sq + (valid ? row : 0)) * D + t * DP;
+    load_dp<DP>(qrow, q);
+    if (!valid)
 #pragma unroll
-    for (int e = 0; e < DP; e += 4) {
-      const float4 x = valid ? *(const float4*)(qrow + e) : make_float4(0.f, 0.f, 0.f, 0.f);
-      q[e] = x.x; q[e + 1] = x.y; q[e + 2] = x.z; q[e + 3] = x.w;
-    }
+      for (int e = 0; e < DP; ++e) q[e] = 0.f;
   }
 #pragma unroll
   for (int e = 0; e < DP; ++e) acc[e] = 0.f;
@@ -82,13 +111,8 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillParams p) {
 #pragma unroll
     for (int j = 0; j < kKB; ++j) {
       const size_t key = (size_t)min(k0 + j, Skv - 1);  // rows past Skv are masked below
-#pragma unroll
-      for (int e = 0; e < DP; e += 4) {
-        const float4 x = *(const float4*)(kbh + key * D + e);
-        kv[j][e] = x.x; kv[j][e + 1] = x.y; kv[j][e + 2] = x.z; kv[j][e + 3] = x.w;
-        const float4 y = *(const float4*)(vbh + key * D + e);
-        vv[j][e] = y.x; vv[j][e + 1] = y.y; vv[j][e + 2] = y.z; vv[j][e + 3] = y.w;
-      }
+      load_dp<DP>(kbh + key * D, kv[j]);
+      load_dp<DP>(vbh + key * D, vv[j]);
     }
     float s[kKB];
     float bm = -INFINITY;
@@ -142,9 +166,7 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillParams p) {
   }
   const float inv = 1.0f / L;
   float* orow = (float*)p.o + (((size_t)b * p.Hq + h) * Sq + row) * D + t * DP;
-#pragma unroll
-  for (int e = 0; e < DP; e += 4)
-    *(float4*)(orow + e) = make_float4(o[e] * inv, o[e + 1] * inv, o[e + 2] * inv, o[e + 3] * inv);
+  store_dp<DP>(orow, o, inv);
 }
 
 }  // namespace
@@ -153,8 +175,16 @@ hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream)
   dim3 grid((p.Sq + kRowsPerWG - 1) / kRowsPerWG, p.Hq, p.B), block(256);
   if (d == 128)
     hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, p);
-  else
+  else if (d == 64)
     hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, p);
+  else if (d == 32)
+    hipLaunchKernelGGL(prefill_f32_kernel<32>, grid, block, 0, stream, p);
+  else if (d == 96)
+    hipLaunchKernelGGL(prefill_f32_kernel<96>, grid, block, 0, stream, p);
+  else if (d == 256)
+    hipLaunchKernelGGL(prefill_f32_kernel<256>, grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -1,0 +1,300 @@
+// bf16 prefill for the head dims the ping-pong kernel does not provide
+// (d = 32, 96, 256): causal or non-causal MQA/GQA attention with an online
+// softmax, fp32 accumulation, bf16 MFMA for both products.
+//
+// It computes the tiled attention of the "Real-time inference optimisation"
+// page (section "Flash Attention optimisation"): the key/value blocks stream
+// through on-chip memory while a running row maximum and row sum rescale the
+// output accumulator, normalised once at the end; with the causal mask and
+// MQA/GQA head sharing of the FlashRT-HF-kernels page (section "attention
+// optimisation"). One work-group per (128-row query tile, head, sequence).
+// The causal mask is bottom-right aligned (query i sees key j iff
+// j <= i + Skv - Sq), as for the other prefill kernels.
+//
+// gfx950 mapping:
+//   - 4 waves x 32 query rows = a 128-row tile; S^T = K . Q^T and
+//     O^T = V^T . P^T on v_mfma_f32_32x32x16_bf16, Q^T held in registers,
+//     K read from LDS with ds_read_b128 and V^T with ds_read_b64_tr_b16;
+//   - K/V blocks of 64 keys come in by direct-to-LDS loads
+//     (buffer_load_dwordx4 ... lds), double-buffered, one barrier per block;
+//   - LDS rows are padded to a power-of-two number of 16-byte chunks (8 for
+//     d = 32, 16 for d = 96) so the XOR swizzles stay inside the row; the
+//     padding chunks are filled with zeros by out-of-range buffer loads;
+//   - d = 256 needs O^T (128 registers) and Q^T (64) per wave, so it runs one
+//     wave per SIMD with up to 512 registers and 128 KB of LDS per work-group;
+//     d = 32 and 96 run two or more work-groups per CU, whose waves overlap
+//     each other's MFMA and softmax phases.
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kTile = 128;   // query rows per work-group
+constexpr int kKN = 64;      // keys per K/V block
+constexpr float kTau = 8.0f; // lazy rescale threshold (log2 units)
+constexpr int kXcdsHd = 8;
+constexpr int kRsrcW3 = 0x00020000;  // raw buffer, 32-bit data format
+constexpr uint32_t kPadOff = 0x80000000u;  // an offset past any block: the load returns zeros
+
+constexpr int pow2ceil(int x) { int r = 1; while (r < x) r *= 2; return r; }
+
+template <int D>
+struct HdCfg {
+  static constexpr int CH = D / 8;                         // 16-byte chunks per K/V row
+  static constexpr int RP = CH < 8 ? 8 : pow2ceil(CH);     // chunks per LDS row (padded)
+  static constexpr int KS = D / 16;                        // k-steps of S^T
+  static constexpr int DB = D / 32;                        // 32-dim blocks of O^T
+  static constexpr int NI = kKN * RP / 64 / 4;             // direct-to-LDS loads per wave per block
+  static constexpr int STAGE = kKN * RP * 8;               // bf16 elements per LDS stage of K or V
+  static constexpr int OCC = D > 128 ? 1 : 2;              // waves per SIMD the registers allow
+};
+
+// K rows are read 16 bytes per lane for 32 consecutive rows at one chunk:
+// XOR with row mod RP spreads 8 consecutive rows over 8 distinct chunks.
+template <int D>
+__device__ __forceinline__ int hswz_k(int row) { return row & (HdCfg<D>::RP - 1); }
+// V^T transpose reads: each 16-lane group reads 4 consecutive rows x 32
+// bytes; an even XOR keeps each 32-byte chunk pair together and places the
+// 4 rows in different bank windows.
+template <int D>
+__device__ __forceinline__ int hswz_v(int row) { return (HdCfg<D>::RP >= 16 ? 4 : 2) * (row & 3); }
+
+__device__ __forceinline__ float hpair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float hpair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+typedef __bf16 hbf16x2 __attribute__((ext_vector_type(2)));
+typedef float hf32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t hpack(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((hf32x2){a, b}, hbf16x2));
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HdCfg<D>::OCC, HdCfg<D>::OCC)))
+prefill_hd_kernel(PrefillParams p) {
+  using C = HdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) __bf16 sK0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ln = lane & 31;
+
+  // Work item I: query tile fastest (most keys first when causal), then
+  // query head, then sequence; each XCD takes a contiguous range of items,
+  // so the query heads of one kv head share that XCD's L2.
+  int t, h, b;
+  {
+    const int W = p.nT * p.Hq * p.B;
+    const int L = blockIdx.x;
+    const int xcd = L % kXcdsHd, idx = L / kXcdsHd;
+    const int qq = W / kXcdsHd, rr = W % kXcdsHd;
+    const int I = (xcd < rr) ? xcd * (qq + 1) + idx : rr * (qq + 1) + (xcd - rr) * qq + idx;
+    t = p.nT - 1 - I % p.nT;
+    h = (I / p.nT) % p.Hq;
+    b = I / (p.nT * p.Hq);
+  }
+  const int g = (int)((long)h * p.Hkv / p.Hq);
+  const int Sq = p.Sq, Skv = p.Skv, off = Skv - Sq;
+  const bool causal = p.causal != 0;
+  const float c = p.c;
+
+  const int q_last = min(t * kTile + kTile, Sq) - 1;           // last row of the tile
+  const int kend = causal ? min(Skv, q_last + off + 1) : Skv;  // keys the tile sees
+  const int nblk = (kend + kKN - 1) / kKN;
+
+  const __bf16* kbh = (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* vbh = (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* qbh = (const __bf16*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
+
+  // Direct-to-LDS offsets: LDS chunk P of a block holds logical chunk
+  // (P % RP) ^ swz(row) of row P / RP; a padding chunk (logical >= CH) gets
+  // an out-of-range offset and is written as zeros.
+  uint32_t koff[C::NI], voff[C::NI];
+#pragma unroll
+  for (int ii = 0; ii < C::NI; ++ii) {
+    const int P = 64 * (wave * C::NI + ii) + lane;
+    const int row = P / C::RP, pc = P % C::RP;
+    const int lk = pc ^ hswz_k<D>(row), lv = pc ^ hswz_v<D>(row);
+    koff[ii] = lk < C::CH ? (uint32_t)(row * D * 2 + lk * 16) : kPadOff;
+    voff[ii] = lv < C::CH ? (uint32_t)(row * D * 2 + lv * 16) : kPadOff;
+  }
+  auto dma = [&](const __bf16* src, __bf16* stage, const uint32_t* offs, int j) __attribute__((always_inline)) {
+    const int kv0 = j * kKN;
+    const int rows = min(kKN, Skv - kv0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kRsrcW3);
+#pragma unroll
+    for (int ii = 0; ii < C::NI; ++ii)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + 64 * (wave * C::NI + ii) * 8), 16,
+                                               (int)offs[ii], 0, 0, 0);
+  };
+
+  // Q^T operand: lane holds Q[row ln][16 ks + 8 hl .. +8] for every k-step;
+  // a negative scale is applied by flipping the sign bits (exact).
+  const uint32_t qflip = p.neg ? 0x80008000u : 0u;
+  const int qrow = t * kTile + wave * 32 + ln;
+  bf16x8 qreg[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (qrow < Sq) x = *(const uint4*)(qbh + (size_t)qrow * D + 16 * ks + 8 * hl);
+    x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
+    qreg[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+
+  f32x16 O[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) O[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kr0 = ln * (C::RP * 16), kr1 = (32 + ln) * (C::RP * 16);
+  const int sw0 = hswz_k<D>(ln), sw1 = hswz_k<D>(32 + ln);
+  auto kread = [&](const char* kb, int kr, int sw, int ks) __attribute__((always_inline)) {
+    return *(const bf16x8*)(kb + kr + (((2 * ks + hl) ^ sw) << 4));
+  };
+  // V^T operand: lane (group gg = lane/16, j = lane%16) reads 8 bytes of rows
+  // 32 sub + 16 s + 4 hl + j/4 and +8, at dims 32 db + 16 (gg%2) + 4 (j%4).
+  const int gg = lane >> 4, jj = lane & 15, dh = gg & 1;
+  auto vread = [&](const char* vb, int sub, int s, int db) __attribute__((always_inline)) {
+    const int row1 = 32 * sub + 16 * s + 4 * hl + (jj >> 2);
+    const int row2 = row1 + 8;
+    const int colb = (32 * db + 16 * dh + 4 * (jj & 3)) * 2;
+    const char* a1 = vb + row1 * (C::RP * 16) + (((colb >> 4) ^ hswz_v<D>(row1)) << 4) + (colb & 15);
+    const char* a2 = vb + row2 * (C::RP * 16) + (((colb >> 4) ^ hswz_v<D>(row2)) << 4) + (colb & 15);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  if (nblk > 0) {
+    dma(kbh, sK0, koff, 0);
+    dma(vbh, sV0, voff, 0);
+  }
+  const int q0 = t * kTile + wave * 32;
+  for (int j = 0; j < nblk; ++j) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block j
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
+    __syncthreads();
+    const bool odd = j & 1;
+    if (j + 1 < nblk) {
+      dma(kbh, odd ? sK0 : sK1, koff, j + 1);
+      dma(vbh, odd ? sV0 : sV1, voff, j + 1);
+    }
+    const int kv0 = j * kKN;
+    // a causal block above every row of this wave contributes nothing
+    if (causal && kv0 > q0 + 31 + off) continue;
+    const char* kb = (const char*)(odd ? sK1 : sK0);
+    const char* vb = (const char*)(odd ? sV1 : sV0);
+
+    f32x16 S0 = f32x16{}, S1 = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kb, kr0, sw0, ks), qreg[ks], S0, 0, 0, 0);
+      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kb, kr1, sw1, ks), qreg[ks], S1, 0, 0, 0);
+    }
+    // key of register r of sub-tile u is kv0 + 32u + 4hl + 8(r/4) + r%4;
+    // visible iff < Skv and (non-causal or) <= query row + off
+    const bool full = kv0 + kKN <= Skv && (!causal || kv0 + kKN - 1 <= q0 + off);
+    if (!full) {
+      const int kb0 = kv0 + 4 * hl;
+      int lim = Skv - 1 - kb0;
+      if (causal) lim = min(lim, q0 + ln + off - kb0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ko = 8 * (r >> 2) + (r & 3);
+        if (ko > lim) S0[r] = -INFINITY;
+        if (ko + 32 > lim) S1[r] = -INFINITY;
+      }
+    }
+    // running reference: raised to the block's scaled row maximum when that
+    // exceeds it by more than kTau, so every probability stays <= 2^kTau
+    float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+    mx = hpair_max(mx);
+    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+    float alpha = 1.f;
+    if (cand > m_run + kTau) {
+      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
+      m_run = cand;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    bf16x8 P[2][2];
+    float la = 0.f, lb = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      float e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sub ? S1[r] : S0[r], c, -mu));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        uint4 w;
+        w.x = hpack(e[8 * s + 0], e[8 * s + 1]);
+        w.y = hpack(e[8 * s + 2], e[8 * s + 3]);
+        w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
+        w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
+        P[sub][s] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+        for (int r = 0; r < 8; r += 2) {
+          la += e[8 * s + r];
+          lb += e[8 * s + r + 1];
+        }
+      }
+    }
+    l_run = alpha * l_run + (la + lb);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vb, sub, s, db), P[sub][s], O[db], 0, 0, 0);
+  }
+
+  // normalise and store (rows past Sq are not written)
+  const float lt = hpair_sum(l_run);
+  const float inv = 1.0f / lt;
+  if (qrow < Sq) {
+    __bf16* dst = (__bf16*)p.o + (((size_t)b * p.Hq + h) * Sq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        uint2 w;
+        w.x = hpack(O[db][4 * rg + 0] * inv, O[db][4 * rg + 1] * inv);
+        w.y = hpack(O[db][4 * rg + 2] * inv, O[db][4 * rg + 3] * inv);
+        *(uint2*)(dst + 32 * db + 8 * rg + 4 * hl) = w;
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) {
+  dim3 grid(p.nT * p.Hq * p.B), block(256);
+  if (d == 32)
+    hipLaunchKernelGGL(prefill_hd_kernel<32>, grid, block, 0, stream, p);
+  else if (d == 96)
+    hipLaunchKernelGGL(prefill_hd_kernel<96>, grid, block, 0, stream, p);
+  else if (d == 256)
+    hipLaunchKernelGGL(prefill_hd_kernel<256>, grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace fa

@@ -351,6 +351,37 @@ def main():
             "note": "chunk of Sq new queries per sequence over its paged cache (chunk included); 100 back-to-back calls"}
         del pq, pk, pv, plens, pbt, po
 
+        # head dims 256 and 96 (their own kernel): back-to-back calls, as above
+        hd = {}
+        for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96()):
+            hq_, hk_, hv_ = bf16(hc.q), bf16(hc.k), bf16(hc.v)
+            ho = torch.empty_like(hq_)
+            hargs = (ctypes.c_void_p(hq_.data_ptr()), ctypes.c_void_p(hk_.data_ptr()), ctypes.c_void_p(hv_.data_ptr()),
+                     ctypes.c_void_p(ho.data_ptr()), hc.B, hc.Hq, hc.Hkv, hc.Sq, hc.Skv, hc.d, hc.scale, 1,
+                     ctypes_stream)
+
+            def hcall(hargs=hargs):
+                st = L.fa_prefill(*hargs)
+                if st != 0:
+                    raise RuntimeError(fa.status_string(st))
+            for _ in range(200):
+                hcall()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(100):
+                hcall()
+            ev1.record(stream)
+            ev1.synchronize()
+            h_us = ev0.elapsed_time(ev1) * 1e3 / 100
+            h_flop = prefill_flops(hc.B, hc.Hq, hc.Sq, hc.Skv, hc.d, True)
+            hd[hc.name] = {"us_per_call_mean": round(h_us, 2), "TFLOP_per_s": round(h_flop / (h_us * 1e-6) / 1e12, 1),
+                           "frac_of_bf16_peak": round(h_flop / (h_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "algorithmic_flop_per_call": h_flop, "B": hc.B, "Hq": hc.Hq, "Hkv": hc.Hkv, "Sq": hc.Sq,
+                           "d": hc.d, "causal": True, "kernel": f"prefill_hd_kernel<{hc.d}>"}
+            del hq_, hk_, hv_, ho
+        result["prefill_head_dims"] = hd
+
         # fp32 single-head causal prefill at B=1 (launch-latency bound)
         c1 = workloads.prefill_f32_small()
         q1 = torch.from_numpy(c1.q).to(dev)

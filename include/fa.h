@@ -83,12 +83,16 @@ int fa_version(void);
  * FlashRT-HF-kernels page).
  *
  *   q, o : bf16 [B, Hq,  Sq,  d]     k, v : bf16 [B, Hkv, Skv, d]
- *   d    : 64 or 128 (FA_ERR_UNSUPPORTED otherwise)
+ *   d    : 32, 64, 96, 128 or 256 (FA_ERR_UNSUPPORTED otherwise)
  *   scale: multiplier of q.k (normally 1/sqrt(d)); must be finite
  *   causal: 0 or 1; bottom-right aligned (see above)
  *
  * QK^T and PV run on bf16 MFMA with fp32 accumulation; the probabilities are
  * rounded to bf16 before the PV product; o is rounded to bf16 (RNE).
+ * d = 64 and 128 run on the two-group ping-pong kernel; d = 32, 96 and 256
+ * on a one-group kernel (one 128-row query tile per work-group, 64-key K/V
+ * blocks double-buffered in LDS; d = 256 at one wave per SIMD for its 128
+ * accumulator registers).
  * o must not alias q, k or v.
  */
 fa_status fa_prefill(const void* q, const void* k, const void* v, void* o,
@@ -98,7 +102,7 @@ fa_status fa_prefill(const void* q, const void* k, const void* v, void* o,
 /*
  * fa_prefill_f32 - the same operation with fp32 q, k, v, o and fp32 arithmetic
  * throughout (no bf16 rounding anywhere). Same arguments and layouts as
- * fa_prefill; d is 64 or 128.
+ * fa_prefill; d is 32, 64, 96, 128 or 256.
  */
 fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
                          int B, int Hq, int Hkv, int Sq, int Skv, int d,
@@ -122,9 +126,9 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
  *                 j <= i + seqlens[b] - Sq (the new tokens are the last Sq);
  *                 a row that sees no token (seqlens[b] < Sq) gives zeros.
  *                 0 -> every row sees all seqlens[b] tokens (zeros if none).
- *   scale, d, stream, errors : as for fa_prefill (d = 64 or 128), plus
- *                 FA_ERR_NULL for a NULL seqlens and FA_ERR_UNSUPPORTED for a
- *                 page size other than 16.
+ *   scale, stream, errors : as for fa_prefill, plus FA_ERR_NULL for a
+ *                 NULL seqlens and FA_ERR_UNSUPPORTED for a page size other
+ *                 than 16 or a d other than 64 and 128.
  * The same kernel as fa_prefill computes it, with one query tile per
  * work-group (the sequences' tiles ordered by cached length, longest first),
  * so with a cache holding exactly fa_prefill's K and V the two agree to

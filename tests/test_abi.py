@@ -48,12 +48,27 @@ def prefill(fn="fa_prefill", q=A, k=A, v=A, o=A, B=1, Hq=4, Hkv=2, Sq=8, Skv=8, 
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(o=None), NULL),
     (dict(B=0), SHAPE), (dict(Hq=0), SHAPE), (dict(Hkv=0), SHAPE), (dict(Sq=0), SHAPE), (dict(Skv=-1), SHAPE),
     (dict(Hq=6, Hkv=4), SHAPE), (dict(Sq=9, Skv=8, causal=1), SHAPE), (dict(B=70000), SHAPE),
-    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(d=0), SHAPE),
+    (dict(d=48), UNSUP), (dict(d=80), UNSUP), (dict(d=512), UNSUP), (dict(d=0), SHAPE),
     (dict(scale=float("inf")), ARG), (dict(scale=float("nan")), ARG), (dict(causal=2), ARG),
     (dict(q=A + 8), ALIGN), (dict(k=A + 4), ALIGN), (dict(v=A + 2), ALIGN), (dict(o=A + 1), ALIGN),
 ])
 def test_prefill_rejects(fn, kw, code):
     assert prefill(fn, **kw) == code
+
+
+def prefill_cache(q=A, kc=A, vc=A, bt=None, lens=A, o=A, B=2, Hq=4, Hkv=2, Sq=8, d=128, L=64, page=16, scale=0.1,
+                  causal=1):
+    return fa.lib().fa_prefill_cache(q, kc, vc, bt, lens, o, B, Hq, Hkv, Sq, d, L, page, scale, causal, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=None), NULL), (dict(q=None), NULL), (dict(Sq=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE),
+    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(d=32), UNSUP), (dict(bt=A, page=32), UNSUP),
+    (dict(causal=2), ARG), (dict(scale=float("nan")), ARG), (dict(lens=A + 2), ALIGN), (dict(bt=A + 1), ALIGN),
+])
+def test_prefill_cache_rejects(kw, code):
+    """Host-side checks of fa_prefill_cache (the cache variant provides d = 64 and 128)."""
+    assert prefill_cache(**kw) == code
 
 
 def decode(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, page=16, tps=0, scale=0.1,

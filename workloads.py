@@ -118,6 +118,18 @@ def prefill_gqa_2k() -> PrefillCase:
                         name="prefill_gqa_b1h32x8s2048d128")
 
 
+def prefill_gqa_d256() -> PrefillCase:
+    """bf16 GQA causal prefill at head dim 256: B=1, Hq=16, Hkv=8, Sq=Skv=2048, scale 1/16."""
+    return prefill_case(1, 16, 8, 2048, 2048, 256, True, "bf16", seed=1007, scale=1.0 / 16.0,
+                        name="prefill_gqa_b1h16x8s2048d256")
+
+
+def prefill_mha_d96() -> PrefillCase:
+    """bf16 MHA causal prefill at head dim 96: B=1, Hq=Hkv=32, Sq=Skv=2048, scale 1/sqrt(96)."""
+    return prefill_case(1, 32, 32, 2048, 2048, 96, True, "bf16", seed=1008, scale=1.0 / math.sqrt(96),
+                        name="prefill_mha_b1h32s2048d96")
+
+
 # --------------------------------------------------------------------------- decode
 
 
