@@ -37,7 +37,7 @@ fa_status check_prefill(const void* q, const void* k, const void* v, void* o, in
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
   // the bf16 kernels run one work-group per (pair of 128-row query tiles, or
   // one tile for the other head dims, head, batch)
-  const long tiles = ((long)Sq + 127) / 128;
+  const long tiles = ((long)Sq + 63) / 64;  // (64-row tiles at d = 256 on small grids)
   if (tiles * Hq * B > (long)INT32_MAX) return FA_ERR_SHAPE;
   return FA_OK;
 }
@@ -116,6 +116,7 @@ fa_status fa_prefill(const void* q, const void* k, const void* v, void* o, int B
   if (st != FA_OK) return st;
   fa::PrefillParams p = make_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, scale, causal);
   if (d == 64 || d == 128) return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+  p.cus = resident_split_groups() / 2;
   return from_hip(fa::launch_prefill_hd(p, d, (hipStream_t)stream));
 }
 

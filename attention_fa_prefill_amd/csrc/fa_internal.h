@@ -35,6 +35,7 @@ struct PrefillParams {
   const int32_t* lens = nullptr;
   const int32_t* bt = nullptr;  // block table [B, pps] or nullptr (contiguous cache)
   int max_len = 0, pps = 0;
+  int cus = 0;  // compute units of the device (head dim 256 picks its kernel by grid size)
 };
 
 hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream);

@@ -23,7 +23,10 @@
 //   - d = 256 needs O^T (128 registers) and Q^T (64) per wave, so it runs one
 //     wave per SIMD with up to 512 registers and 128 KB of LDS per work-group;
 //     d = 32 and 96 run two or more work-groups per CU, whose waves overlap
-//     each other's MFMA and softmax phases.
+//     each other's MFMA and softmax phases;
+//   - d = 256 grids of fewer than two rounds of 128-row tiles (one work-group
+//     per CU) run prefill_hd_ks_kernel instead: 64-row tiles whose keys are
+//     split between two wave pairs (below).
 #include "fa_internal.h"
 
 namespace fa {
@@ -282,6 +285,232 @@ prefill_hd_kernel(PrefillParams p) {
   }
 }
 
+// d = 256 with the keys of each tile split between two wave pairs: a
+// work-group owns a 64-row query tile; waves 2kh and 2kh+1 own its two 32-row
+// halves over the 32-key blocks kh, kh+2, kh+4, ... (kh = 0, 1), and the two
+// partial states of each row are merged through LDS at the end. Against one
+// wave per 32 rows over all keys this halves the longest chain of blocks in a
+// causal grid, and the 64-row tiles (twice as many work-groups, most keys
+// first) fill the CUs in two balanced rounds where 128-row tiles made one
+// unbalanced round.
+constexpr int kTileKs = 64;  // query rows per work-group
+constexpr int kKBKs = 32;    // keys per block
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+prefill_hd_ks_kernel(PrefillParams p) {
+  using C = HdCfg<D>;
+  constexpr int STG = kKBKs * C::RP * 8;      // bf16 elements of one 32-key block
+  constexpr int NIK = kKBKs * C::RP / 64 / 2; // direct-to-LDS loads per wave per block (two waves share it)
+  // [stage][key half]; the merge reuses this memory
+  __shared__ __attribute__((aligned(1024))) __bf16 sK[2][2][STG];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV[2][2][STG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ln = lane & 31;
+  const int rh = wave & 1, kh = wave >> 1;  // row half, key half
+
+  const int nT = (p.Sq + kTileKs - 1) / kTileKs;
+  int t, h, b;
+  {
+    const int W = nT * p.Hq * p.B;
+    const int L = blockIdx.x;
+    const int xcd = L % kXcdsHd, idx = L / kXcdsHd;
+    const int qq = W / kXcdsHd, rr = W % kXcdsHd;
+    const int I = (xcd < rr) ? xcd * (qq + 1) + idx : rr * (qq + 1) + (xcd - rr) * qq + idx;
+    t = nT - 1 - I % nT;
+    h = (I / nT) % p.Hq;
+    b = I / (nT * p.Hq);
+  }
+  const int g = (int)((long)h * p.Hkv / p.Hq);
+  const int Sq = p.Sq, Skv = p.Skv, off = Skv - Sq;
+  const bool causal = p.causal != 0;
+  const float c = p.c;
+  const int q_last = min(t * kTileKs + kTileKs, Sq) - 1;
+  const int kend = causal ? min(Skv, q_last + off + 1) : Skv;
+  const int nb = (kend + kKBKs - 1) / kKBKs;  // 32-key blocks the tile sees
+  const int iters = (nb + 1) / 2;
+
+  const __bf16* kbh = (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* vbh = (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* qbh = (const __bf16*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
+
+  // this wave loads rows 16 rh .. 16 rh + 15 of its key half's blocks
+  uint32_t koff[NIK], voff[NIK];
+#pragma unroll
+  for (int ii = 0; ii < NIK; ++ii) {
+    const int P = 64 * (NIK * rh + ii) + lane;
+    const int row = P / C::RP, pc = P % C::RP;
+    const int lk = pc ^ hswz_k<D>(row), lv = pc ^ hswz_v<D>(row);
+    koff[ii] = lk < C::CH ? (uint32_t)(row * D * 2 + lk * 16) : kPadOff;
+    voff[ii] = lv < C::CH ? (uint32_t)(row * D * 2 + lv * 16) : kPadOff;
+  }
+  auto dma = [&](const __bf16* src, __bf16* stage, const uint32_t* offs, int jb) __attribute__((always_inline)) {
+    const int kv0 = jb * kKBKs;
+    const int rows = min(kKBKs, Skv - kv0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kRsrcW3);
+#pragma unroll
+    for (int ii = 0; ii < NIK; ++ii)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + 64 * (NIK * rh + ii) * 8), 16,
+                                               (int)offs[ii], 0, 0, 0);
+  };
+
+  const uint32_t qflip = p.neg ? 0x80008000u : 0u;
+  const int q0 = t * kTileKs + rh * 32;
+  const int qrow = q0 + ln;
+  bf16x8 qreg[C::KS];
+#pragma unroll
+  for (int ks = 0; ks < C::KS; ++ks) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (qrow < Sq) x = *(const uint4*)(qbh + (size_t)qrow * D + 16 * ks + 8 * hl);
+    x.x ^= qflip; x.y ^= qflip; x.z ^= qflip; x.w ^= qflip;
+    qreg[ks] = __builtin_bit_cast(bf16x8, x);
+  }
+
+  f32x16 O[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) O[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kr0 = ln * (C::RP * 16);
+  const int sw0 = hswz_k<D>(ln);
+  const int gg = lane >> 4, jj = lane & 15, dh = gg & 1;
+  auto vread = [&](const char* vb, int s, int db) __attribute__((always_inline)) {
+    const int row1 = 16 * s + 4 * hl + (jj >> 2);
+    const int row2 = row1 + 8;
+    const int colb = (32 * db + 16 * dh + 4 * (jj & 3)) * 2;
+    const char* a1 = vb + row1 * (C::RP * 16) + (((colb >> 4) ^ hswz_v<D>(row1)) << 4) + (colb & 15);
+    const char* a2 = vb + row2 * (C::RP * 16) + (((colb >> 4) ^ hswz_v<D>(row2)) << 4) + (colb & 15);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  if (kh < nb) {
+    dma(kbh, sK[0][kh], koff, kh);
+    dma(vbh, sV[0][kh], voff, kh);
+  }
+  for (int i = 0; i < iters; ++i) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of its block
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
+    __syncthreads();
+    const int st = i & 1;
+    const int jn = 2 * (i + 1) + kh;
+    if (jn < nb) {
+      dma(kbh, sK[st ^ 1][kh], koff, jn);
+      dma(vbh, sV[st ^ 1][kh], voff, jn);
+    }
+    const int jb = 2 * i + kh;
+    const int kv0 = jb * kKBKs;
+    if (jb >= nb || (causal && kv0 > q0 + 31 + off)) continue;
+    const char* kb = (const char*)sK[st][kh];
+    const char* vb = (const char*)sV[st][kh];
+
+    f32x16 S = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kb + kr0 + (((2 * ks + hl) ^ sw0) << 4)),
+                                                 qreg[ks], S, 0, 0, 0);
+    // key of register r is kv0 + 4hl + 8(r/4) + r%4
+    const bool full = kv0 + kKBKs <= Skv && (!causal || kv0 + kKBKs - 1 <= q0 + off);
+    if (!full) {
+      const int kb0 = kv0 + 4 * hl;
+      int lim = Skv - 1 - kb0;
+      if (causal) lim = min(lim, qrow + off - kb0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) S[r] = -INFINITY;
+    }
+    float mx = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    mx = hpair_max(mx);
+    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+    float alpha = 1.f;
+    if (cand > m_run + kTau) {
+      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
+      m_run = cand;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    float e[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c, -mu));
+    bf16x8 P[2];
+    float la = 0.f, lb = 0.f;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 w;
+      w.x = hpack(e[8 * s + 0], e[8 * s + 1]);
+      w.y = hpack(e[8 * s + 2], e[8 * s + 3]);
+      w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
+      w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
+      P[s] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+      for (int r = 0; r < 8; r += 2) {
+        la += e[8 * s + r];
+        lb += e[8 * s + r + 1];
+      }
+    }
+    l_run = alpha * l_run + (la + lb);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vb, s, db), P[s], O[db], 0, 0, 0);
+  }
+
+  // merge the key halves: the kh = 1 waves hand (m, l, O) to the kh = 0 waves
+  // of the same rows through LDS (the stages are free once every wave is here)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  float4* xo = (float4*)&sK[0][0][0] + rh * (C::DB * 4 * 64);  // 32 KB per row half
+  float* xm = (float*)&sV[0][0][0] + rh * 128;
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg)
+        xo[(db * 4 + rg) * 64 + lane] =
+            make_float4(O[db][4 * rg], O[db][4 * rg + 1], O[db][4 * rg + 2], O[db][4 * rg + 3]);
+    xm[lane] = m_run;
+    xm[64 + lane] = l_run;
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float m1 = xm[lane], l1 = xm[64 + lane];
+    const float M = fmaxf(m_run, m1);  // finite: every row sees key 0 in block 0
+    const float f0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+    const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+    const float lt = hpair_sum(l_run * f0 + l1 * f1);
+    const float inv = 1.0f / lt;
+    if (qrow < Sq) {
+      __bf16* dst = (__bf16*)p.o + (((size_t)b * p.Hq + h) * Sq + qrow) * D;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const float4 o1 = xo[(db * 4 + rg) * 64 + lane];
+          const float v0 = (O[db][4 * rg + 0] * f0 + o1.x * f1) * inv;
+          const float v1 = (O[db][4 * rg + 1] * f0 + o1.y * f1) * inv;
+          const float v2 = (O[db][4 * rg + 2] * f0 + o1.z * f1) * inv;
+          const float v3 = (O[db][4 * rg + 3] * f0 + o1.w * f1) * inv;
+          uint2 w;
+          w.x = hpack(v0, v1);
+          w.y = hpack(v2, v3);
+          *(uint2*)(dst + 32 * db + 8 * rg + 4 * hl) = w;
+        }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) {
@@ -290,6 +519,11 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
     hipLaunchKernelGGL(prefill_hd_kernel<32>, grid, block, 0, stream, p);
   else if (d == 96)
     hipLaunchKernelGGL(prefill_hd_kernel<96>, grid, block, 0, stream, p);
+  else if (d == 256 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
+    // fewer than two rounds of 128-row tiles at one work-group per CU: the
+    // key-split kernel's 64-row tiles balance the CUs better
+    hipLaunchKernelGGL(prefill_hd_ks_kernel<256>, dim3(((p.Sq + kTileKs - 1) / kTileKs) * p.Hq * p.B), block, 0,
+                       stream, p);
   else if (d == 256)
     hipLaunchKernelGGL(prefill_hd_kernel<256>, grid, block, 0, stream, p);
   else

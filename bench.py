@@ -352,6 +352,12 @@ def main():
         del pq, pk, pv, plens, pbt, po
 
         # head dims 256 and 96 (their own kernel): back-to-back calls, as above
+        n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+        def hd_kernel_name(hc):
+            # d = 256 grids under two rounds of 128-row tiles take the key-split kernel
+            tiles = -(-hc.Sq // 128) * hc.Hq * hc.B
+            return "prefill_hd_ks_kernel<256>" if hc.d == 256 and tiles < 2 * n_cus else f"prefill_hd_kernel<{hc.d}>"
         hd = {}
         for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96()):
             hq_, hk_, hv_ = bf16(hc.q), bf16(hc.k), bf16(hc.v)
@@ -378,7 +384,7 @@ def main():
             hd[hc.name] = {"us_per_call_mean": round(h_us, 2), "TFLOP_per_s": round(h_flop / (h_us * 1e-6) / 1e12, 1),
                            "frac_of_bf16_peak": round(h_flop / (h_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "algorithmic_flop_per_call": h_flop, "B": hc.B, "Hq": hc.Hq, "Hkv": hc.Hkv, "Sq": hc.Sq,
-                           "d": hc.d, "causal": True, "kernel": f"prefill_hd_kernel<{hc.d}>"}
+                           "d": hc.d, "causal": True, "kernel": hd_kernel_name(hc)}
             del hq_, hk_, hv_, ho
         result["prefill_head_dims"] = hd
 

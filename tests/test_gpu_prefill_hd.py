@@ -60,6 +60,12 @@ SHAPES = [
     (1, 2, 1, 128, 4096, 32, False),     # long KV
     (1, 2, 1, 33, 4000, 256, True),
     (1, 3, 1, 65, 191, 96, False),
+    # d = 256 grids of at least two rounds of 128-row tiles (512 on 256 CUs)
+    # take the one-group kernel, smaller ones the key-split kernel
+    (4, 16, 8, 1024, 1024, 256, True),
+    (2, 32, 4, 1000, 900, 256, False),
+    (1, 8, 2, 1500, 1500, 256, True),
+    (1, 2, 1, 2, 777, 256, False),
 ]
 
 
