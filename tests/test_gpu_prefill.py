@@ -85,6 +85,27 @@ def test_fp32_shapes(shape):
     assert_f32_close(host_f64(o), oracle_out(case), case.name)
 
 
+CROSS = [
+    # cross-attention: the queries of one sequence over the keys and values of
+    # another (an encoder's output), non-causal, Sq != Skv
+    # B, Hq, Hkv, Sq, Skv, d
+    (2, 8, 8, 77, 1500, 64),     # decoder tokens over a long encoder output
+    (1, 16, 16, 448, 1500, 64),
+    (3, 4, 4, 1024, 77, 128),    # many queries over a short context
+    (1, 12, 12, 333, 257, 96),
+    (2, 8, 4, 150, 600, 256),
+]
+
+
+@pytest.mark.parametrize("shape", CROSS, ids=lambda s: "b{}h{}x{}sq{}skv{}d{}".format(*s))
+def test_bf16_cross_attention(shape):
+    B, Hq, Hkv, Sq, Skv, d = shape
+    case = workloads.prefill_case(B, Hq, Hkv, Sq, Skv, d, False, "bf16", seed=4000 + Sq + Skv + d,
+                                  name=f"cross_b{B}h{Hq}x{Hkv}sq{Sq}skv{Skv}d{d}")
+    o, _ = run_case(case)
+    assert_bf16_close(host_f64(o), oracle_out(case), case.name)
+
+
 @pytest.mark.parametrize("scale", [-0.09, 0.0, 0.5])
 def test_bf16_scale_sign_and_zero(scale):
     case = workloads.prefill_case(1, 4, 2, 150, 150, 128, True, "bf16", seed=321, scale=scale)
