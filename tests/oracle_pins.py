@@ -193,7 +193,8 @@ def pin_torch_sdpa(lib=None):
     import torch
 
     for (B, Hq, Hkv, Sq, Skv, d, causal) in ((1, 1, 1, 128, 128, 64, True), (2, 4, 2, 33, 33, 16, True),
-                                             (1, 4, 1, 7, 19, 8, False), (2, 2, 2, 16, 16, 32, False)):
+                                             (1, 4, 1, 7, 19, 8, False), (2, 2, 2, 16, 16, 32, False),
+                                             (1, 2, 1, 40, 40, 96, True), (1, 2, 2, 9, 70, 256, False)):
         q, k, v = _rand((B, Hq, Sq, d), 31), _rand((B, Hkv, Skv, d), 32), _rand((B, Hkv, Skv, d), 33)
         o, _ = oracle.attention(q, k, v, 1.0 / math.sqrt(d), causal, lib=lib)
         G = Hq // Hkv
