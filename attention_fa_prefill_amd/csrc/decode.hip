@@ -53,19 +53,19 @@ constexpr float kTau = 8.0f;   // lazy rescale threshold (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// V staging swizzle: 16-byte chunk XOR 2*(row % 8) (D=128) / 2*(row % 4) (D=64),
+// V staging swizzle: 16-byte chunk XOR 2*(row % 8) (D=128, 256) / 2*(row % 4) (D=64),
 // so the 4-row x 32-byte footprint of each transpose read hits distinct banks.
 template <int D>
-__device__ __forceinline__ int swz_v(int row) { return 2 * (row & (D == 128 ? 7 : 3)); }
+__device__ __forceinline__ int swz_v(int row) { return 2 * (row & (D >= 128 ? 7 : 3)); }
 // FP8 V staging swizzle. A transpose read of 8-bit elements (ds_read_b64_tr_b8)
 // by 16 lanes covers one 16-byte chunk of 8 rows: tokens 4cq..4cq+3 and
 // 16+4cq..16+4cq+3 of the step. XOR with a function of the row that differs
-// on those 8 rows (D=128: 8 chunks per row) or, with the row's parity, still
-// separates them (D=64: 4 chunks per 64-byte row) places the 8 reads in
-// distinct banks.
+// on those 8 rows (D=128, 256: 8 or 16 chunks per row) or, with the row's
+// parity, still separates them (D=64: 4 chunks per 64-byte row) places the 8
+// reads in distinct banks.
 template <int D>
 __device__ __forceinline__ int swz_v8(int row) {
-  return D == 128 ? ((row & 3) | (((row >> 4) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 4) & 1) << 1));
+  return D >= 128 ? ((row & 3) | (((row >> 4) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 4) & 1) << 1));
 }
 
 // Waits for this wave's vector-memory loads (direct-to-LDS included) until at
@@ -431,19 +431,26 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   KReg kA[2][KS], kB[2][KS];
   __bf16* stA = sV0[w];
   __bf16* stB = sV1[w];
+  // (d = 256: a step is 32 loads, so before a new step's loads go out the
+  // pending ones are brought down to 31; the count never exceeds the 63 the
+  // wait counter holds)
+  constexpr int kRoom = 2 * NLD > 63 ? 63 - NLD : -1;
   dma_v(w, stA);
   load_k(w, kA);
+  if constexpr (kRoom >= 0) wait_vm<kRoom>();
   dma_v(w + 4, stB);
   load_k(w + 4, kB);
   for (int i = 0; i < nw; i += 2) {
     wait_vm<NLD>();  // step i's loads are done; step i+1's may be pending
     step(w + 4 * i, kA, stA);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's reads of stage A are done
+    if constexpr (kRoom >= 0) wait_vm<kRoom>();
     dma_v(w + 4 * (i + 2), stA);
     load_k(w + 4 * (i + 2), kA);
     wait_vm<NLD>();
     if (i + 1 < nw) step(w + 4 * (i + 1), kB, stB);
     __builtin_amdgcn_s_waitcnt(0xC07F);
+    if constexpr (kRoom >= 0) wait_vm<kRoom>();
     dma_v(w + 4 * (i + 3), stB);
     load_k(w + 4 * (i + 3), kB);
   }
@@ -601,10 +608,16 @@ hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t str
     hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, block, 0, stream, p);
   else if (d == 64 && !fp8)
     hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, block, 0, stream, p);
+  else if (d == 256 && !fp8)
+    hipLaunchKernelGGL((decode_split_kernel<256, false>), grid, block, 0, stream, p);
   else if (d == 128)
     hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, block, 0, stream, p);
-  else
+  else if (d == 64)
     hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, block, 0, stream, p);
+  else if (d == 256)
+    hipLaunchKernelGGL((decode_split_kernel<256, true>), grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeParams m;
@@ -627,8 +640,12 @@ hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream) {
   dim3 grid(p.R, d / 32), block(256);
   if (d == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, p);
-  else
+  else if (d == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, p);
+  else if (d == 256)
+    hipLaunchKernelGGL(merge_kernel<256>, grid, block, 0, stream, p);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

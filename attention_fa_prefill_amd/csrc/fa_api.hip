@@ -180,7 +180,7 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   if (!q || !kcache || !vcache || !seqlens || !o) return FA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_kv_len <= 0) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   if (block_table && page_size != 16) return FA_ERR_UNSUPPORTED;
   const int tps = fa_decode_split_tokens(B, Hq, Hkv, max_kv_len, tokens_per_split);
   if (tps <= 0) return FA_ERR_ARG;
@@ -207,7 +207,8 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   p.hchunks = hchunks;
   p.compact = B <= kCompactMaxB ? 1 : 0;
   p.adapt = (tokens_per_split == 0 && p.compact) ? 1 : 0;
-  p.cap = resident_split_groups();
+  // (d = 256: one split work-group per CU, its registers and LDS allow no second)
+  p.cap = d == 256 ? resident_split_groups() / 2 : resident_split_groups();
   // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0;
   // an fp8 K scale multiplies every score, so it joins c
   p.c = fmaxf(fabsf(scale) * (fp8 ? k_scale : 1.0f) * fa::kLog2e, 1e-30f);
@@ -243,7 +244,7 @@ fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* l
                        int out_bf16, void* stream) {
   if (!o_parts || !lse || !o) return FA_ERR_NULL;
   if (R <= 0 || S <= 0 || d <= 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   if (!aligned16(o_parts) || !aligned16(o) || !aligned4(lse) || (lse_out && !aligned4(lse_out)))
     return FA_ERR_ALIGN;
   fa::MergeParams m;

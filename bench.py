@@ -177,9 +177,8 @@ def main():
             times.append(a.elapsed_time(b) * 1e3)
         return times
 
-    def decode_leg():
+    def decode_leg(makers=(workloads.decode_contig_32k, workloads.decode_paged_mixed, workloads.decode_long_256k)):
         dec = {}
-        makers = (workloads.decode_contig_32k, workloads.decode_paged_mixed, workloads.decode_long_256k)
         cases = [m() for m in makers] + [workloads.as_fp8(m()) for m in makers]
         for dc in cases:
             if dc.fp8:  # FP8 E4M3 codes, one byte per element
@@ -387,6 +386,10 @@ def main():
                            "d": hc.d, "causal": True, "kernel": hd_kernel_name(hc)}
             del hq_, hk_, hv_, ho
         result["prefill_head_dims"] = hd
+
+        # decode at head dim 256 (one split work-group per CU), bf16 and FP8
+        # caches, timed like the decode legs above
+        result["decode_head_dim_256"] = decode_leg(makers=(workloads.decode_paged_d256,))
 
         # fp32 single-head causal prefill at B=1 (launch-latency bound)
         c1 = workloads.prefill_f32_small()

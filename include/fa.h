@@ -189,7 +189,7 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, 
  *                 at most 2048.
  *   workspace   : device scratch of at least fa_decode_workspace_bytes(...)
  *                 bytes, 16-byte aligned; contents undefined after the call.
- *   d           : 64 or 128.  Hq / Hkv query heads share one kv head.
+ *   d           : 64, 128 or 256.  Hq / Hkv query heads share one kv head.
  *
  * Two kernels run in stream order: a split-KV kernel writing per-split
  * (normalised output, log-sum-exp), then the log-sum-exp merge into o.
@@ -239,7 +239,7 @@ fa_status fa_decode_fp8(const void* q, const void* kcache, const void* vcache,
  *   lse     : fp32 [R, S] natural-log log-sum-exp of each part's scores
  *   o       : [R, d], bf16 when out_bf16 != 0, else fp32
  *   lse_out : fp32 [R] or NULL
- *   d       : 64 or 128
+ *   d       : 64, 128 or 256
  */
 fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* lse_out,
                        int R, int S, int d, int out_bf16, void* stream);

@@ -82,7 +82,8 @@ def decode(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, p
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(lens=None), NULL), (dict(o=None), NULL),
     (dict(B=0, wsb=1 << 20), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(L=0, wsb=1 << 20), SHAPE),
     (dict(Hkv=0), SHAPE),
-    (dict(d=80), UNSUP), (dict(bt=A, page=32), UNSUP), (dict(bt=A, page=8), UNSUP),
+    (dict(d=80), UNSUP), (dict(d=96), UNSUP), (dict(d=512), UNSUP), (dict(bt=A, page=32), UNSUP),
+    (dict(bt=A, page=8), UNSUP),
     (dict(tps=48), ARG), (dict(tps=-32), ARG), (dict(tps=4096), ARG), (dict(scale=float("nan")), ARG),
     (dict(q=A + 2), ALIGN), (dict(k=A + 8), ALIGN), (dict(o=A + 4), ALIGN), (dict(lens=A + 2), ALIGN),
     (dict(bt=A + 1), ALIGN), (dict(ws=A + 8), ALIGN),
@@ -151,7 +152,7 @@ def test_decode_workspace_bytes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(op=None), NULL), (dict(lse=None), NULL), (dict(o=None), NULL),
-    (dict(R=0), SHAPE), (dict(S=0), SHAPE), (dict(d=32), UNSUP),
+    (dict(R=0), SHAPE), (dict(S=0), SHAPE), (dict(d=32), UNSUP), (dict(d=96), UNSUP), (dict(d=512), UNSUP),
     (dict(op=A + 4), ALIGN), (dict(o=A + 8), ALIGN), (dict(lse=A + 2), ALIGN), (dict(lo=A + 1), ALIGN),
 ])
 def test_merge_rejects(kw, code):

@@ -235,6 +235,13 @@ def decode_long_256k(poison=False) -> DecodeCase:
                         name="decode_long_b1h16x2kv256kd128", poison=poison)
 
 
+def decode_paged_d256(poison=False) -> DecodeCase:
+    """Decode at head dim 256: B=4, Hq=16, Hkv=8, mixed lengths U{1024..16384},
+    page 16, shuffled pool (GQA with two query heads per kv head)."""
+    return decode_paged(4, 16, 8, 256, paged_lengths(1009, 4, 1024, 16384), 16384, seed=1009,
+                        name="decode_paged_b4h16x8kv1k16kd256", poison=poison)
+
+
 def paged_from_contiguous(case: DecodeCase, seed: int = 99) -> DecodeCase:
     """Scatter a contiguous cache into a shuffled page pool (same values, same
     lengths): the paged view of exactly the same data."""
