@@ -99,7 +99,7 @@ const char* fa_status_string(fa_status s) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (<= 0, Hq % Hkv != 0, causal with Sq > Skv, or too large)";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim must be 64 or 128 and page_size 16";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim or page_size not provided (prefill d = 32, 64, 96, 128, 256; chunked prefill 64, 128; decode 64, 128, 256; page_size 16)";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
