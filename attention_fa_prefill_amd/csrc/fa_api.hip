@@ -99,7 +99,7 @@ const char* fa_status_string(fa_status s) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (<= 0, Hq % Hkv != 0, causal with Sq > Skv, or too large)";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim or page_size not provided (prefill d = 32, 64, 96, 128, 256; chunked prefill 64, 128; decode 64, 128, 256; page_size 16)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim or page_size not provided (prefill d = 32, 64, 96, 128, 256; decode 64, 128, 256; page_size 16)";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
@@ -128,7 +128,6 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
   // Sq <= Skv (here a row with no visible key gives zeros)
   fa_status st = check_prefill(q, kcache, vcache, o, B, Hq, Hkv, Sq, max_kv_len, d, scale, 0);
   if (st != FA_OK) return st;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (block_table && page_size != 16) return FA_ERR_UNSUPPORTED;
   if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
@@ -142,7 +141,8 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
   p.bt = block_table;
   p.max_len = max_kv_len;
   p.pps = (max_kv_len + 15) / 16;
-  return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+  if (d == 64 || d == 128) return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+  return from_hip(fa::launch_prefill_hd(p, d, (hipStream_t)stream));
 }
 
 fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv, int Sq,

@@ -77,7 +77,13 @@ __device__ __forceinline__ uint32_t hpack(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((hf32x2){a, b}, hbf16x2));
 }
 
-template <int D>
+// CACHE: K and V come from a KV cache in the decode layouts (contiguous
+// [B, max_len, Hkv, D] or pages of 16 tokens through a block table) with
+// Skv = seqlens[b]: the chunked prefill, whose Sq new queries are the last Sq
+// cached tokens (bottom-right causal alignment); a row with no visible key
+// gives zeros. Each wave's loads of a 64-key block cover exactly its 16 rows,
+// one page, read through one buffer resource bounded at the last valid key.
+template <int D, bool CACHE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HdCfg<D>::OCC, HdCfg<D>::OCC)))
 prefill_hd_kernel(PrefillParams p) {
   using C = HdCfg<D>;
@@ -105,35 +111,53 @@ prefill_hd_kernel(PrefillParams p) {
     b = I / (p.nT * p.Hq);
   }
   const int g = (int)((long)h * p.Hkv / p.Hq);
-  const int Sq = p.Sq, Skv = p.Skv, off = Skv - Sq;
+  const int Sq = p.Sq;
+  const int Skv = CACHE ? min(max(p.lens[b], 0), p.max_len) : p.Skv;
+  const int off = Skv - Sq;
   const bool causal = p.causal != 0;
   const float c = p.c;
 
   const int q_last = min(t * kTile + kTile, Sq) - 1;           // last row of the tile
-  const int kend = causal ? min(Skv, q_last + off + 1) : Skv;  // keys the tile sees
-  const int nblk = (kend + kKN - 1) / kKN;
+  const int kend = causal ? min(Skv, q_last + off + 1) : Skv;  // keys the tile sees (CACHE: maybe none)
+  const int nblk = max(0, (kend + kKN - 1) / kKN);
 
-  const __bf16* kbh = (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
-  const __bf16* vbh = (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* kbh = CACHE ? (const __bf16*)p.k : (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* vbh = CACHE ? (const __bf16*)p.v : (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const uint32_t rowstride = CACHE ? (uint32_t)p.Hkv * D * 2u : (uint32_t)D * 2u;
   const __bf16* qbh = (const __bf16*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
 
   // Direct-to-LDS offsets: LDS chunk P of a block holds logical chunk
   // (P % RP) ^ swz(row) of row P / RP; a padding chunk (logical >= CH) gets
   // an out-of-range offset and is written as zeros.
+  // (CACHE: wave w's chunks are rows 16 w .. 16 w + 15 of the block, one
+  // page; offsets are relative to that page's first row)
   uint32_t koff[C::NI], voff[C::NI];
 #pragma unroll
   for (int ii = 0; ii < C::NI; ++ii) {
     const int P = 64 * (wave * C::NI + ii) + lane;
     const int row = P / C::RP, pc = P % C::RP;
     const int lk = pc ^ hswz_k<D>(row), lv = pc ^ hswz_v<D>(row);
-    koff[ii] = lk < C::CH ? (uint32_t)(row * D * 2 + lk * 16) : kPadOff;
-    voff[ii] = lv < C::CH ? (uint32_t)(row * D * 2 + lv * 16) : kPadOff;
+    const uint32_t rb = (uint32_t)(CACHE ? (row & 15) : row) * rowstride;
+    koff[ii] = lk < C::CH ? rb + (uint32_t)(lk * 16) : kPadOff;
+    voff[ii] = lv < C::CH ? rb + (uint32_t)(lv * 16) : kPadOff;
   }
   auto dma = [&](const __bf16* src, __bf16* stage, const uint32_t* offs, int j) __attribute__((always_inline)) {
     const int kv0 = j * kKN;
-    const int rows = min(kKN, Skv - kv0);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kRsrcW3);
+    __amdgpu_buffer_rsrc_t rs;
+    if constexpr (CACHE) {
+      const int r0 = kv0 + 16 * wave;
+      const int nvalid = max(0, min(16, Skv - r0));
+      const char* base = (const char*)src;
+      if (nvalid > 0) {
+        const long prow = p.bt ? (long)p.bt[(size_t)b * p.pps + r0 / 16] * 16 : (long)b * p.max_len + r0;
+        base += ((size_t)prow * p.Hkv + g) * (size_t)(D * 2);
+      }
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                             nvalid > 0 ? (nvalid - 1) * (int)rowstride + D * 2 : 0, kRsrcW3);
+    } else {
+      const int rows = min(kKN, Skv - kv0);
+      rs = __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kRsrcW3);
+    }
 #pragma unroll
     for (int ii = 0; ii < C::NI; ++ii)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + 64 * (wave * C::NI + ii) * 8), 16,
@@ -268,9 +292,10 @@ prefill_hd_kernel(PrefillParams p) {
           O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vb, sub, s, db), P[sub][s], O[db], 0, 0, 0);
   }
 
-  // normalise and store (rows past Sq are not written)
+  // normalise and store (rows past Sq are not written; CACHE: a row with no
+  // visible key has l = 0 and gives zeros)
   const float lt = hpair_sum(l_run);
-  const float inv = 1.0f / lt;
+  const float inv = CACHE ? (lt > 0.f ? 1.0f / lt : 0.f) : 1.0f / lt;
   if (qrow < Sq) {
     __bf16* dst = (__bf16*)p.o + (((size_t)b * p.Hq + h) * Sq + qrow) * D;
 #pragma unroll
@@ -514,18 +539,30 @@ prefill_hd_ks_kernel(PrefillParams p) {
 }  // namespace
 
 hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) {
-  dim3 grid(p.nT * p.Hq * p.B), block(256);
+  const dim3 grid(p.nT * p.Hq * p.B), block(256);
+  if (p.lens) {
+    // chunked prefill over a KV cache: the one-group kernel
+    if (d == 32)
+      hipLaunchKernelGGL((prefill_hd_kernel<32, true>), grid, block, 0, stream, p);
+    else if (d == 96)
+      hipLaunchKernelGGL((prefill_hd_kernel<96, true>), grid, block, 0, stream, p);
+    else if (d == 256)
+      hipLaunchKernelGGL((prefill_hd_kernel<256, true>), grid, block, 0, stream, p);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
+  // d = 256 grids of fewer than two rounds of 128-row tiles (one work-group
+  // per CU) take the key-split kernel, whose 64-row tiles balance the CUs
   if (d == 32)
-    hipLaunchKernelGGL(prefill_hd_kernel<32>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_hd_kernel<32, false>), grid, block, 0, stream, p);
   else if (d == 96)
-    hipLaunchKernelGGL(prefill_hd_kernel<96>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_hd_kernel<96, false>), grid, block, 0, stream, p);
   else if (d == 256 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
-    // fewer than two rounds of 128-row tiles at one work-group per CU: the
-    // key-split kernel's 64-row tiles balance the CUs better
     hipLaunchKernelGGL(prefill_hd_ks_kernel<256>, dim3(((p.Sq + kTileKs - 1) / kTileKs) * p.Hq * p.B), block, 0,
                        stream, p);
   else if (d == 256)
-    hipLaunchKernelGGL(prefill_hd_kernel<256>, grid, block, 0, stream, p);
+    hipLaunchKernelGGL((prefill_hd_kernel<256, false>), grid, block, 0, stream, p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -126,14 +126,17 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
  *                 j <= i + seqlens[b] - Sq (the new tokens are the last Sq);
  *                 a row that sees no token (seqlens[b] < Sq) gives zeros.
  *                 0 -> every row sees all seqlens[b] tokens (zeros if none).
- *   scale, stream, errors : as for fa_prefill, plus FA_ERR_NULL for a
- *                 NULL seqlens and FA_ERR_UNSUPPORTED for a page size other
- *                 than 16 or a d other than 64 and 128.
- * The same kernel as fa_prefill computes it, with one query tile per
- * work-group (the sequences' tiles ordered by cached length, longest first),
- * so with a cache holding exactly fa_prefill's K and V the two agree to
- * rounding. For the same seqlens the paged and contiguous caches give
- * bitwise equal results.
+ *   scale, d, stream, errors : as for fa_prefill (d = 32, 64, 96, 128 or
+ *                 256), plus FA_ERR_NULL for a NULL seqlens and
+ *                 FA_ERR_UNSUPPORTED for a page size other than 16.
+ * The same kernels as fa_prefill compute it. At d = 64 and 128 the ping-pong
+ * kernel takes one query tile per work-group (the sequences' tiles ordered
+ * by cached length, longest first), so with a cache holding exactly
+ * fa_prefill's K and V the two agree to rounding; at d = 32, 96 and 256 the
+ * one-group kernel runs as for fa_prefill (at d = 32 and 96 with the same
+ * bits; d = 256 may differ from fa_prefill's key-split kernel by rounding).
+ * For the same seqlens the paged and contiguous caches give bitwise equal
+ * results.
  */
 fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache,
                            const int32_t* block_table, const int32_t* seqlens, void* o,

@@ -63,11 +63,11 @@ def prefill_cache(q=A, kc=A, vc=A, bt=None, lens=A, o=A, B=2, Hq=4, Hkv=2, Sq=8,
 
 @pytest.mark.parametrize("kw,code", [
     (dict(lens=None), NULL), (dict(q=None), NULL), (dict(Sq=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE),
-    (dict(d=96), UNSUP), (dict(d=256), UNSUP), (dict(d=32), UNSUP), (dict(bt=A, page=32), UNSUP),
+    (dict(d=48), UNSUP), (dict(d=80), UNSUP), (dict(d=512), UNSUP), (dict(bt=A, page=32), UNSUP),
     (dict(causal=2), ARG), (dict(scale=float("nan")), ARG), (dict(lens=A + 2), ALIGN), (dict(bt=A + 1), ALIGN),
 ])
 def test_prefill_cache_rejects(kw, code):
-    """Host-side checks of fa_prefill_cache (the cache variant provides d = 64 and 128)."""
+    """Host-side checks of fa_prefill_cache."""
     assert prefill_cache(**kw) == code
 
 

@@ -114,3 +114,67 @@ def test_many_sequences_mixed_lengths(B):
     got = host_f64(run(case))
     assert_bf16_close(got, oracle_out(case), f"B={B}")
     assert np.all(got[lens == 0] == 0.0)
+
+
+# ---------------------------------------------------------------- head dims 32, 96, 256
+SHAPES_HD = [
+    # B, Hq, Hkv, Sq, d, lens, max_kv_len, paged, causal
+    (2, 8, 2, 128, 96, [1000, 129], 1024, True, True),
+    (3, 4, 1, 200, 256, [200, 1500, 333], 1536, True, True),     # MQA, Sq not a tile multiple
+    (2, 4, 4, 300, 32, [700, 301], 704, False, True),
+    (1, 16, 8, 640, 256, [3000], 3008, True, True),
+    (2, 2, 1, 256, 96, [100, 0], 256, True, True),                # L < Sq and L = 0: zero rows
+    (2, 8, 2, 96, 256, [50, 1000], 1024, False, False),           # non-causal
+    (4, 4, 2, 64, 32, [64, 65, 1, 17], 80, True, False),
+    (2, 12, 12, 333, 96, [2000, 333], 2048, True, True),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES_HD, ids=lambda s: "b{}h{}x{}sq{}d{}kv{}{}{}".format(
+    s[0], s[1], s[2], s[3], s[4], s[6], "p" if s[7] else "c", "c" if s[8] else "n"))
+def test_head_dim_shapes(shape):
+    B, Hq, Hkv, Sq, d, lens, mkl, paged, causal = shape
+    case = workloads.prefill_cache_case(B, Hq, Hkv, Sq, d, lens, mkl, paged=paged, causal=causal,
+                                        seed=sum(lens) % 1000 + Sq + d)
+    got = host_f64(run(case))
+    assert_bf16_close(got, oracle_out(case), case.name)
+    for b, L in enumerate(lens):
+        if causal and L < Sq:
+            assert np.all(got[b, :, : Sq - L] == 0.0)
+        if L == 0:
+            assert np.all(got[b] == 0.0)
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_head_dim_paged_equals_contiguous_bitwise(d):
+    case = workloads.prefill_cache_case(2, 8, 4, 200, d, [1024, 555], 1024, paged=False, causal=True, seed=80 + d)
+    B, L = case.B, case.max_kv_len
+    perm = np.random.default_rng(10).permutation(B * (L // 16))
+    bt = perm.reshape(B, L // 16).astype(np.int32)
+    kp = np.empty((B * (L // 16), 16, case.Hkv, case.d), np.uint16)
+    vp = np.empty_like(kp)
+    kp[bt.reshape(-1)] = case.kcache.reshape(-1, 16, case.Hkv, case.d)
+    vp[bt.reshape(-1)] = case.vcache.reshape(-1, 16, case.Hkv, case.d)
+    paged = dataclasses.replace(case, kcache=kp, vcache=vp, block_table=bt, name=case.name + "_paged")
+    assert np.array_equal(host_bits(run(case)), host_bits(run(paged)))
+
+
+@pytest.mark.parametrize("d", [96, 256])
+def test_head_dim_poisoned_slots_do_not_leak(d):
+    lens = [1000, 17, 512]
+    clean = workloads.prefill_cache_case(3, 4, 2, 256, d, lens, 1024, paged=True, seed=74 + d)
+    dirty = workloads.prefill_cache_case(3, 4, 2, 256, d, lens, 1024, paged=True, seed=74 + d, poison=True)
+    o_dirty = run(dirty)
+    assert np.all(np.isfinite(host_f64(o_dirty)))
+    assert np.array_equal(host_bits(o_dirty), host_bits(run(clean)))
+
+
+def test_head_dim_96_full_cache_equals_prefill_bitwise():
+    """At d = 96 the cache variant is the same one-group kernel as fa_prefill,
+    with the same tile order and key blocks, so a contiguous cache holding
+    prefill's K and V gives the same bits."""
+    case = workloads.prefill_cache_case(2, 8, 2, 700, 96, [1100, 1100], 1100, paged=False, causal=True, seed=75)
+    k = dev_bf16(case.kcache).permute(0, 2, 1, 3).contiguous()
+    v = dev_bf16(case.vcache).permute(0, 2, 1, 3).contiguous()
+    o_plain = fa.prefill(dev_bf16(case.q), k, v, causal=True, scale=case.scale)
+    assert np.array_equal(host_bits(run(case)), host_bits(o_plain))
