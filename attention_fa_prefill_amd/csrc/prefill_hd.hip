@@ -36,6 +36,7 @@ constexpr int kTile = 128;   // query rows per work-group
 constexpr int kKN = 64;      // keys per K/V block
 constexpr float kTau = 8.0f; // lazy rescale threshold (log2 units)
 constexpr int kXcdsHd = 8;
+constexpr int kRankMaxBHd = 512;  // sequences ordered by length in every work-group up to this batch
 constexpr int kRsrcW3 = 0x00020000;  // raw buffer, 32-bit data format
 constexpr uint32_t kPadOff = 0x80000000u;  // an offset past any block: the load returns zeros
 
@@ -100,7 +101,42 @@ prefill_hd_kernel(PrefillParams p) {
   // query head, then sequence; each XCD takes a contiguous range of items,
   // so the query heads of one kv head share that XCD's L2.
   int t, h, b;
-  {
+  if constexpr (CACHE && C::OCC > 1) {
+    // With a cache a tile's cost is its sequence's cached length. The
+    // (sequence, kv head) groups are ordered by descending length and dealt
+    // whole, round-robin, to the 8 XCDs (each XCD gets an equal mix of long
+    // and short sequences, longest first, and keeps a kv head's K/V in one
+    // L2); inside a group, tiles by descending causal cost, then heads.
+    // (d = 256, one work-group per CU, keeps the plain order below: measured
+    // faster there on mixed lengths.)
+    const int G = p.Hq / p.Hkv;
+    const int per_group = G * p.nT;
+    const int xcd = (int)blockIdx.x % kXcdsHd, idx = (int)blockIdx.x / kXcdsHd;
+    const int k = xcd + kXcdsHd * (idx / per_group);
+    if (k >= p.B * p.Hkv) return;  // past this XCD's groups (uniform)
+    const int within = idx % per_group;
+    const int r = k / p.Hkv;
+    h = (k % p.Hkv) * G + within % G;
+    t = p.nT - 1 - within / G;
+    // the sequence of length rank r (longest first, ties by index); beyond
+    // kRankMaxBHd sequences, index order
+    b = r;
+    if (p.B <= kRankMaxBHd) {
+      int* rank_slot = (int*)sK0;  // not in use yet
+      for (int u0 = tid; u0 < p.B; u0 += 256) {
+        const int lt = min(max(p.lens[u0], 0), p.max_len);
+        int rank = 0;
+        for (int u = 0; u < p.B; ++u) {
+          const int lu = min(max(p.lens[u], 0), p.max_len);
+          rank += (lu > lt || (lu == lt && u < u0)) ? 1 : 0;
+        }
+        if (rank == r) *rank_slot = u0;
+      }
+      __syncthreads();
+      b = __builtin_amdgcn_readfirstlane(*rank_slot);
+      __syncthreads();  // every wave has read the slot before sK0 is loaded
+    }
+  } else {
     const int W = p.nT * p.Hq * p.B;
     const int L = blockIdx.x;
     const int xcd = L % kXcdsHd, idx = L / kXcdsHd;
@@ -541,11 +577,16 @@ prefill_hd_ks_kernel(PrefillParams p) {
 hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) {
   const dim3 grid(p.nT * p.Hq * p.B), block(256);
   if (p.lens) {
-    // chunked prefill over a KV cache: the one-group kernel
+    // chunked prefill over a KV cache: the one-group kernel, one work-group
+    // per (query tile, head, sequence), padded to whole rounds of (sequence,
+    // kv head) groups on the 8 XCDs
+    // (d = 32, 96: padded to whole rounds of (sequence, kv head) groups on the
+    // 8 XCDs, longest sequences first; d = 256: the plain grid)
+    const dim3 grid_c(kXcdsHd * ((p.B * p.Hkv + kXcdsHd - 1) / kXcdsHd) * (p.Hq / p.Hkv) * p.nT);
     if (d == 32)
-      hipLaunchKernelGGL((prefill_hd_kernel<32, true>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((prefill_hd_kernel<32, true>), grid_c, block, 0, stream, p);
     else if (d == 96)
-      hipLaunchKernelGGL((prefill_hd_kernel<96, true>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((prefill_hd_kernel<96, true>), grid_c, block, 0, stream, p);
     else if (d == 256)
       hipLaunchKernelGGL((prefill_hd_kernel<256, true>), grid, block, 0, stream, p);
     else
