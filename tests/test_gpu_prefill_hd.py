@@ -15,7 +15,7 @@ import pytest
 import attention_fa_prefill_amd as fa
 import oracle
 import workloads
-from tests.gpu_util import (assert_bf16_close, assert_f32_close, dev_bf16, dev_f32, host_bits, host_f64,
+from tests.gpu_util import (assert_bf16_close, assert_f32_close, dev_bf16, dev_f32, dev_i32, host_bits, host_f64,
                             torch_gpu)
 
 pytestmark = pytest.mark.gpu
@@ -137,3 +137,71 @@ def test_output_canary_untouched(d):
     torch.cuda.synchronize()
     assert torch.all(buf[:1024] == 1234.0) and torch.all(buf[1024 + n:] == 1234.0)
     assert_bf16_close(host_f64(o), oracle_out(case), case.name)
+
+
+@pytest.mark.parametrize("d,B", [(128, 1), (256, 1), (256, 4), (96, 1)])
+def test_graph_capture_replays(d, B):
+    """fa_prefill captured in a HIP graph (the ping-pong kernel at d = 128, the
+    key-split and one-group kernels at d = 256, the one-group kernel at d = 96):
+    every replay, with eager work between replays and new q written in place,
+    equals the eager call bit for bit."""
+    torch = torch_gpu()
+    case = workloads.prefill_case(B, 16, 8, 1024, 1024, d, True, "bf16", seed=500 + d + B)
+    q, k, v = dev_bf16(case.q), dev_bf16(case.k), dev_bf16(case.v)
+    o = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fa.prefill(q, k, v, o, causal=True, scale=case.scale)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fa.prefill(q, k, v, o, causal=True, scale=case.scale)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        if rep % 2 == 1:
+            q.copy_(torch.randn(q.shape, device="cuda").to(torch.bfloat16))
+        x = torch.randn(1 << 20, device="cuda")
+        (x * 2 + 1).sum().item()  # eager work between replays
+        print(f"replay {rep} d={d} B={B}", flush=True)
+        g.replay()
+        torch.cuda.synchronize()
+        ref = fa.prefill(q, k, v, causal=True, scale=case.scale)
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(o), host_bits(ref)), f"replay {rep}"
+
+
+def test_graph_capture_replays_prefill_cache():
+    """fa_prefill_cache (paged, d = 256 and 128) captured in a HIP graph: replays
+    with new lengths written into seqlens equal the eager call bit for bit."""
+    torch = torch_gpu()
+    for d in (256, 128):
+        case = workloads.prefill_cache_case(3, 8, 4, 300, d, [1200, 700, 300], 1216, paged=True, causal=True,
+                                            seed=600 + d)
+        q, kc, vc = dev_bf16(case.q), dev_bf16(case.kcache), dev_bf16(case.vcache)
+        lens, bt = dev_i32(case.seqlens), dev_i32(case.block_table)
+        o = torch.empty_like(q)
+
+        def call(out=None):
+            return fa.prefill_cache(q, kc, vc, lens, block_table=bt, max_kv_len=case.max_kv_len, causal=True,
+                                    scale=case.scale, o=out)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(o)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            call(o)
+        torch.cuda.synchronize()
+        for rep, new in enumerate(([1200, 700, 300], [400, 1216, 301], [299, 1, 1000], [1200, 700, 300])):
+            lens.copy_(torch.tensor(new, dtype=torch.int32))
+            (torch.randn(1 << 20, device="cuda") * 2).sum().item()
+            print(f"replay {rep} d={d} lens={new}", flush=True)
+            g.replay()
+            torch.cuda.synchronize()
+            ref = call()
+            torch.cuda.synchronize()
+            assert np.array_equal(host_bits(o), host_bits(ref)), f"d={d} replay {rep}"
