@@ -169,9 +169,238 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillParams p) {
   store_dp<DP>(orow, o, inv);
 }
 
+// ---------------------------------------------------------------------------
+// Large shapes: the same attention on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32, full fp32 products and sums), for d = 32, 64, 96
+// and 128. One work-group of 4 waves per (128-row query tile, head, batch);
+// each wave owns 32 query rows; K and V blocks of 32 keys come into LDS by
+// direct-to-LDS loads, double-buffered, one barrier per block. (d = 128
+// holds 340 registers per lane: one wave per SIMD.)
+//
+// The contraction order is permuted so that every operand comes whole from
+// 16-byte pieces: in k-step (m, e) lane half hl (lanes 32 hl .. 32 hl + 31)
+// contracts index 8m + 4hl + e (e = 0..3). For S^T = K . Q^T the index is a
+// dim: a lane reads dims 8m + 4hl .. +3 of its key with one 16-byte LDS read
+// and holds those of its query in registers. For O^T = V^T . P^T the index is
+// a key: the score accumulator of a lane already holds keys 8m + 4hl + e in
+// its registers 4m + e (the 32x32 output layout), so the probabilities are
+// the B operand in place, in fp32; V^T comes as four 4-byte LDS reads.
+constexpr int kKNf = 32;        // keys per block
+constexpr float kTauF = 8.0f;   // lazy rescale threshold (log2 units)
+constexpr int kXcdsF = 8;
+constexpr int kRsrcW3F = 0x00020000;
+
+template <int D>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 96 ? 1 : 2, D > 96 ? 1 : 2)))
+prefill_f32_mfma_kernel(PrefillParams p) {
+  constexpr int CH = D / 4;              // 16-byte chunks per fp32 row
+  constexpr int STAGE = kKNf * D;        // floats per K or V block
+  constexpr int NI = kKNf * CH / 64 / 4; // direct-to-LDS loads per wave per block
+  constexpr int DB = D / 32;             // 32-dim blocks of O^T
+  constexpr int KM = D / 8;              // groups of 4 k-steps of S^T
+  __shared__ __attribute__((aligned(1024))) float sK0[STAGE];
+  __shared__ __attribute__((aligned(1024))) float sV0[STAGE];
+  __shared__ __attribute__((aligned(1024))) float sK1[STAGE];
+  __shared__ __attribute__((aligned(1024))) float sV1[STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, ln = lane & 31;
+  int t, h, b;
+  {
+    const int W = p.nT * p.Hq * p.B;
+    const int L = blockIdx.x;
+    const int xcd = L % kXcdsF, idx = L / kXcdsF;
+    const int qq = W / kXcdsF, rr = W % kXcdsF;
+    const int I = (xcd < rr) ? xcd * (qq + 1) + idx : rr * (qq + 1) + (xcd - rr) * qq + idx;
+    t = p.nT - 1 - I % p.nT;
+    h = (I / p.nT) % p.Hq;
+    b = I / (p.nT * p.Hq);
+  }
+  const int g = (int)((long)h * p.Hkv / p.Hq);
+  const int Sq = p.Sq, Skv = p.Skv, off = Skv - Sq;
+  const bool causal = p.causal != 0;
+  const float c = p.c;
+  const int q_last = min(t * 128 + 128, Sq) - 1;
+  const int kend = causal ? min(Skv, q_last + off + 1) : Skv;
+  const int nblk = (kend + kKNf - 1) / kKNf;
+
+  const float* kbh = (const float*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const float* vbh = (const float*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const float* qbh = (const float*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
+
+  // LDS chunk P of a block holds logical chunk (P % CH) ^ (row % 8) of row
+  // P / CH (CH is a multiple of 8): the 16-byte K reads of 8 consecutive rows
+  // at one chunk land in 8 distinct bank groups.
+  uint32_t off_[NI];
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int P = 64 * (wave * NI + ii) + lane;
+    const int row = P / CH, pc = P % CH;
+    off_[ii] = (uint32_t)(row * D * 4 + ((pc ^ (row & 7)) << 4));
+  }
+  auto dma = [&](const float* src, float* stage, int j) __attribute__((always_inline)) {
+    const int kv0 = j * kKNf;
+    const int rows = min(kKNf, Skv - kv0);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)kv0 * D), (short)0, rows * D * 4, kRsrcW3F);
+#pragma unroll
+    for (int ii = 0; ii < NI; ++ii)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + 64 * (wave * NI + ii) * 4), 16,
+                                               (int)off_[ii], 0, 0, 0);
+  };
+
+  // Q^T operand: lane (query ln, half hl) holds dims 8m + 4hl .. +3 of its row;
+  // a negative scale flips the sign here (exact), so c >= 0.
+  const int qrow = t * 128 + wave * 32 + ln;
+  const float qs = p.neg ? -1.f : 1.f;
+  float4 qreg[KM];
+#pragma unroll
+  for (int m = 0; m < KM; ++m) {
+    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (qrow < Sq) x = *(const float4*)(qbh + (size_t)qrow * D + 8 * m + 4 * hl);
+    qreg[m] = make_float4(x.x * qs, x.y * qs, x.z * qs, x.w * qs);
+  }
+
+  f32x16 O[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) O[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int q0 = t * 128 + wave * 32;
+
+  if (nblk > 0) {
+    dma(kbh, sK0, 0);
+    dma(vbh, sV0, 0);
+  }
+  for (int j = 0; j < nblk; ++j) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block j
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
+    __syncthreads();
+    const bool odd = j & 1;
+    if (j + 1 < nblk) {
+      dma(kbh, odd ? sK0 : sK1, j + 1);
+      dma(vbh, odd ? sV0 : sV1, j + 1);
+    }
+    const int kv0 = j * kKNf;
+    if (causal && kv0 > q0 + 31 + off) continue;  // above every row of this wave
+    const char* kb = (const char*)(odd ? sK1 : sK0);
+    const float* vb = odd ? sV1 : sV0;
+
+    // S^T (32 keys x 32 queries): lane (query ln, half hl) register r holds
+    // key kv0 + 8 (r / 4) + 4 hl + r % 4
+    // two accumulation chains (even and odd m), added at the end: half the
+    // sequential rounding of one chain over all d products
+    // two accumulation chains (even and odd m), added at the end: half the
+    // sequential rounding of one chain over all d products
+    f32x16 S = f32x16{}, S2 = f32x16{};
+#pragma unroll
+    for (int m = 0; m < KM; ++m) {
+      const float4 kx = *(const float4*)(kb + ln * (D * 4) + (((2 * m + hl) ^ (ln & 7)) << 4));
+      f32x16& A = (m & 1) ? S2 : S;
+      A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.x, qreg[m].x, A, 0, 0, 0);
+      A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.y, qreg[m].y, A, 0, 0, 0);
+      A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.z, qreg[m].z, A, 0, 0, 0);
+      A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.w, qreg[m].w, A, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] += S2[r];
+    const bool full = kv0 + kKNf <= Skv && (!causal || kv0 + kKNf - 1 <= q0 + off);
+    if (!full) {
+      const int kb0 = kv0 + 4 * hl;
+      int lim = Skv - 1 - kb0;
+      if (causal) lim = min(lim, qrow + off - kb0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) > lim) S[r] = -INFINITY;
+    }
+    float mx = S[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+    float alpha = 1.f;
+    if (cand > m_run + kTauF) {
+      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
+      m_run = cand;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    float ls = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      S[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c, -mu));
+      ls += S[r];
+    }
+    l_run = alpha * l_run + ls;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
+    }
+    // O^T += V^T . P^T: k-step (m, e) contracts key 8m + 4hl + e, whose
+    // probability is this lane's register 4m + e
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 8 * m + 4 * hl + e;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int dim = 32 * db + ln;
+          const float vx = vb[row * D + ((((dim >> 2) ^ (row & 7))) << 2) + (dim & 3)];
+          O[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vx, S[4 * m + e], O[db], 0, 0, 0);
+        }
+      }
+      // the V reads of the next 4 keys are not hoisted above this point, which
+      // bounds the registers they hold
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // normalise and store: lane (query ln, half hl) register r of O[db] holds
+  // dim 32 db + 8 (r / 4) + 4 hl + r % 4
+  float lt;
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+    lt = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  const float inv = 1.0f / lt;
+  if (qrow < Sq) {
+    float* dst = (float*)p.o + (((size_t)b * p.Hq + h) * Sq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        *(float4*)(dst + 32 * db + 8 * a4 + 4 * hl) =
+            make_float4(O[db][4 * a4] * inv, O[db][4 * a4 + 1] * inv, O[db][4 * a4 + 2] * inv,
+                        O[db][4 * a4 + 3] * inv);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream) {
+  // Grids of at least 128 query tiles of 128 rows (over heads and batch) take
+  // the matrix-core kernel (d <= 128); smaller ones, bound by launch latency
+  // or by too few work-groups for the CUs, take the vector kernel, whose
+  // work-groups own 4 rows each.
+  if (d <= 128 && (long)p.nT * p.Hq * p.B >= 128) {
+    const dim3 grid(p.nT * p.Hq * p.B), block(256);
+    if (d == 128)
+      hipLaunchKernelGGL(prefill_f32_mfma_kernel<128>, grid, block, 0, stream, p);
+    else if (d == 64)
+      hipLaunchKernelGGL(prefill_f32_mfma_kernel<64>, grid, block, 0, stream, p);
+    else if (d == 96)
+      hipLaunchKernelGGL(prefill_f32_mfma_kernel<96>, grid, block, 0, stream, p);
+    else if (d == 32)
+      hipLaunchKernelGGL(prefill_f32_mfma_kernel<32>, grid, block, 0, stream, p);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   dim3 grid((p.Sq + kRowsPerWG - 1) / kRowsPerWG, p.Hq, p.B), block(256);
   if (d == 128)
     hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, p);

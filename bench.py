@@ -41,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz)
+PEAK_FP32_TFLOPS = 157.3  # MI355X dense fp32 (matrix and vector)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "prefill attn TFLOP/s + decode HBM GB/s (% of peak); µs/call at B=1"
 PREFILL_KERNEL_SRC = os.path.join(ROOT, "attention_fa_prefill_amd", "csrc", "prefill_bf16.hip")
@@ -386,6 +387,37 @@ def main():
                            "d": hc.d, "causal": True, "kernel": hd_kernel_name(hc)}
             del hq_, hk_, hv_, ho
         result["prefill_head_dims"] = hd
+
+        # fp32 prefill at the C2 shape (the matrix-core fp32 kernel), timed like
+        # the head-dim legs, against the fp32 matrix peak
+        fc = workloads.prefill_case(1, 32, 8, 2048, 2048, 128, True, "f32", seed=1002, scale=128 ** -0.5,
+                                    name="prefill_f32_gqa_b1h32x8s2048d128")
+        fq, fk, fv = (torch.from_numpy(x).to(dev) for x in (fc.q, fc.k, fc.v))
+        fo = torch.empty_like(fq)
+        fargs = (ctypes.c_void_p(fq.data_ptr()), ctypes.c_void_p(fk.data_ptr()), ctypes.c_void_p(fv.data_ptr()),
+                 ctypes.c_void_p(fo.data_ptr()), 1, 32, 8, 2048, 2048, 128, fc.scale, 1, ctypes_stream)
+
+        def fcall():
+            st = L.fa_prefill_f32(*fargs)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+        for _ in range(30):
+            fcall()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(30):
+            fcall()
+        ev1.record(stream)
+        ev1.synchronize()
+        f_us = ev0.elapsed_time(ev1) * 1e3 / 30
+        f_flop = prefill_flops(1, 32, 2048, 2048, 128, True)
+        result["prefill_f32_large"] = {
+            "workload": fc.name, "us_per_call_mean": round(f_us, 2),
+            "TFLOP_per_s": round(f_flop / (f_us * 1e-6) / 1e12, 2),
+            "frac_of_fp32_peak": round(f_flop / (f_us * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
+            "kernel": "prefill_f32_mfma_kernel<128>", "note": "30 back-to-back calls after 30 warm-up calls"}
+        del fq, fk, fv, fo
 
         # decode at head dim 256 (one split work-group per CU), bf16 and FP8
         # caches, timed like the decode legs above
