@@ -354,9 +354,7 @@ prefill_f32_mfma_kernel(PrefillParams p) {
           O[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vx, S[4 * m + e], O[db], 0, 0, 0);
         }
       }
-      // the V reads of the next 4 keys are not hoisted above this point, which
-      // bounds the registers they hold
-      __builtin_amdgcn_sched_barrier(0);
+
     }
   }
 
