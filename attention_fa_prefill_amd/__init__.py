@@ -108,6 +108,36 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
 
+def _cache_geometry(kcache, vcache, seqlens, block_table, max_kv_len, B, d):
+    """(max_kv_len, page_size) of a contiguous or paged cache, after checking
+    that the tensors agree with each other and with the batch: the kernels use
+    max_kv_len as the per-sequence row count of a contiguous cache and read B
+    lengths and B block-table rows."""
+    if kcache.shape != vcache.shape or kcache.shape[3] != d:
+        raise ValueError("kcache and vcache must match and end in [Hkv, d]")
+    if seqlens.dim() != 1 or seqlens.numel() != B:
+        raise ValueError(f"seqlens must be int32 [B] with B = {B}")
+    if block_table is None:
+        if kcache.shape[0] != B:
+            raise ValueError("contiguous cache must be [B, max_kv_len, Hkv, d]")
+        mkl = kcache.shape[1]
+        if max_kv_len is not None and int(max_kv_len) != mkl:
+            raise ValueError(f"max_kv_len ({max_kv_len}) must equal the contiguous cache's length ({mkl})")
+        return mkl, 0
+    if kcache.shape[1] != 16 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("paged cache must be [num_pages, 16, Hkv, d] with block_table [B, pages]")
+    mkl = 16 * block_table.shape[1] if max_kv_len is None else int(max_kv_len)
+    if (mkl + 15) // 16 != block_table.shape[1]:
+        raise ValueError("block_table must have ceil(max_kv_len/16) columns")
+    return mkl, 16
+
+
+def _check_out(o, q):
+    """A caller's output tensor must match q in shape and dtype."""
+    if o is not None and (o.shape != q.shape or o.dtype != q.dtype):
+        raise ValueError(f"o must match q in shape {tuple(q.shape)} and dtype {q.dtype}")
+
+
 # ----------------------------------------------------------------------------- entry points
 
 
@@ -118,8 +148,6 @@ def prefill(q, k, v, o=None, *, causal: bool = True, scale: float | None = None,
     fp32 runs ``fa_prefill_f32``.
     """
     torch = _torch()
-    _dev(q, k, v, o)
-    _contig(q, k, v, o)
     if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
         raise ValueError("expected q [B,Hq,Sq,d] and k, v [B,Hkv,Skv,d]")
     B, Hq, Sq, d = q.shape
@@ -128,10 +156,11 @@ def prefill(q, k, v, o=None, *, causal: bool = True, scale: float | None = None,
         raise ValueError("q and k/v disagree on batch or head_dim")
     if not (q.dtype == k.dtype == v.dtype) or q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError("q, k, v must all be bfloat16 or all float32")
+    _check_out(o, q)
+    _dev(q, k, v, o)
+    _contig(q, k, v, o)
     if o is None:
         o = torch.empty_like(q)
-    elif o.shape != q.shape or o.dtype != q.dtype:
-        raise ValueError("o must match q in shape and dtype")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     fn = lib().fa_prefill if q.dtype == torch.bfloat16 else lib().fa_prefill_f32
@@ -148,28 +177,18 @@ def prefill_cache(q, kcache, vcache, seqlens, *, block_table=None, max_kv_len: i
     int32 [B, pages_per_seq]); seqlens int32 [B] cached tokens, the new ones
     included. Returns o [B,Hq,Sq,d] bf16."""
     torch = _torch()
-    _dev(q, kcache, vcache, seqlens, block_table, o)
-    _contig(q, kcache, vcache, seqlens, block_table, o)
     if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
         raise ValueError("prefill_cache takes bfloat16 q and caches")
     if seqlens.dtype != torch.int32 or (block_table is not None and block_table.dtype != torch.int32):
         raise ValueError("seqlens and block_table must be int32")
+    if q.dim() != 4 or kcache.dim() != 4:
+        raise ValueError("expected q [B,Hq,Sq,d] and caches of 4 dims")
     B, Hq, Sq, d = q.shape
     Hkv = kcache.shape[2]
-    if kcache.shape != vcache.shape or kcache.shape[3] != d:
-        raise ValueError("kcache and vcache must match and end in [Hkv, d]")
-    if block_table is None:
-        if kcache.shape[0] != B:
-            raise ValueError("contiguous cache must be [B, max_kv_len, Hkv, d]")
-        mkl = kcache.shape[1] if max_kv_len is None else int(max_kv_len)
-        page = 0
-    else:
-        if kcache.shape[1] != 16 or block_table.shape[0] != B:
-            raise ValueError("paged cache must be [num_pages, 16, Hkv, d] with block_table [B, pages]")
-        mkl = 16 * block_table.shape[1] if max_kv_len is None else int(max_kv_len)
-        if (mkl + 15) // 16 != block_table.shape[1]:
-            raise ValueError("block_table must have ceil(max_kv_len/16) columns")
-        page = 16
+    mkl, page = _cache_geometry(kcache, vcache, seqlens, block_table, max_kv_len, B, d)
+    _check_out(o, q)
+    _dev(q, kcache, vcache, seqlens, block_table, o)
+    _contig(q, kcache, vcache, seqlens, block_table, o)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if o is None:
@@ -214,8 +233,6 @@ def decode_fp8(q, kcache, vcache, seqlens, *, k_scale: float, v_scale: float, bl
 def _decode(q, kcache, vcache, seqlens, fp8_scales, block_table, max_kv_len, scale, tokens_per_split, o, workspace,
             stream):
     torch = _torch()
-    _dev(q, kcache, vcache, seqlens, block_table, o, workspace)
-    _contig(q, kcache, vcache, seqlens, block_table, o, workspace)
     if fp8_scales is None:
         if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
             raise ValueError("decode takes bfloat16 q and caches")
@@ -225,22 +242,14 @@ def _decode(q, kcache, vcache, seqlens, fp8_scales, block_table, max_kv_len, sca
             raise ValueError("decode_fp8 takes a bfloat16 q and uint8 / float8_e4m3fn caches")
     if seqlens.dtype != torch.int32 or (block_table is not None and block_table.dtype != torch.int32):
         raise ValueError("seqlens and block_table must be int32")
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("expected q [B,Hq,d] and caches of 4 dims")
     B, Hq, d = q.shape
     Hkv = kcache.shape[2]
-    if kcache.shape != vcache.shape or kcache.shape[3] != d:
-        raise ValueError("kcache and vcache must match and end in [Hkv, d]")
-    if block_table is None:
-        if kcache.shape[0] != B:
-            raise ValueError("contiguous cache must be [B, max_kv_len, Hkv, d]")
-        mkl = kcache.shape[1] if max_kv_len is None else int(max_kv_len)
-        page = 0
-    else:
-        if kcache.shape[1] != 16 or block_table.shape[0] != B:
-            raise ValueError("paged cache must be [num_pages, 16, Hkv, d] with block_table [B, pages]")
-        mkl = 16 * block_table.shape[1] if max_kv_len is None else int(max_kv_len)
-        if (mkl + 15) // 16 != block_table.shape[1]:
-            raise ValueError("block_table must have ceil(max_kv_len/16) columns")
-        page = 16
+    mkl, page = _cache_geometry(kcache, vcache, seqlens, block_table, max_kv_len, B, d)
+    _check_out(o, q)
+    _dev(q, kcache, vcache, seqlens, block_table, o, workspace)
+    _contig(q, kcache, vcache, seqlens, block_table, o, workspace)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if o is None:
@@ -265,13 +274,23 @@ def merge_lse(o_parts, lse, *, out_dtype=None, o=None, lse_out=None, stream=None
     Returns (o [R, d] in out_dtype (bf16 default, or fp32), lse_out fp32 [R]).
     """
     torch = _torch()
-    _dev(o_parts, lse, o, lse_out)
-    _contig(o_parts, lse, o, lse_out)
     if o_parts.dtype != torch.float32 or lse.dtype != torch.float32:
         raise ValueError("o_parts and lse must be float32")
+    if o_parts.dim() != 3:
+        raise ValueError("o_parts must be [R, S, d]")
     R, S, d = o_parts.shape
+    if tuple(lse.shape) != (R, S):
+        raise ValueError(f"lse must be [R, S] = [{R}, {S}]")
     if out_dtype is None:
         out_dtype = torch.bfloat16 if o is None else o.dtype
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("the merged output is bfloat16 or float32")
+    if o is not None and (tuple(o.shape) != (R, d) or o.dtype != out_dtype):
+        raise ValueError(f"o must be [R, d] = [{R}, {d}] of dtype {out_dtype}")
+    if lse_out is not None and (tuple(lse_out.shape) != (R,) or lse_out.dtype != torch.float32):
+        raise ValueError(f"lse_out must be float32 [R] = [{R}]")
+    _dev(o_parts, lse, o, lse_out)
+    _contig(o_parts, lse, o, lse_out)
     if o is None:
         o = torch.empty((R, d), dtype=out_dtype, device=o_parts.device)
     if lse_out is None:

@@ -604,21 +604,21 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
 
 hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream) {
   dim3 grid(p.B * p.nsplit * p.Hkv * p.hchunks), block(256);
+  hipError_t e;
   if (d == 128 && !fp8)
-    hipLaunchKernelGGL((decode_split_kernel<128, false>), grid, block, 0, stream, p);
+    e = launch_kernel(decode_split_kernel<128, false>, grid, block, stream, p);
   else if (d == 64 && !fp8)
-    hipLaunchKernelGGL((decode_split_kernel<64, false>), grid, block, 0, stream, p);
+    e = launch_kernel(decode_split_kernel<64, false>, grid, block, stream, p);
   else if (d == 256 && !fp8)
-    hipLaunchKernelGGL((decode_split_kernel<256, false>), grid, block, 0, stream, p);
+    e = launch_kernel(decode_split_kernel<256, false>, grid, block, stream, p);
   else if (d == 128)
-    hipLaunchKernelGGL((decode_split_kernel<128, true>), grid, block, 0, stream, p);
+    e = launch_kernel(decode_split_kernel<128, true>, grid, block, stream, p);
   else if (d == 64)
-    hipLaunchKernelGGL((decode_split_kernel<64, true>), grid, block, 0, stream, p);
+    e = launch_kernel(decode_split_kernel<64, true>, grid, block, stream, p);
   else if (d == 256)
-    hipLaunchKernelGGL((decode_split_kernel<256, true>), grid, block, 0, stream, p);
+    e = launch_kernel(decode_split_kernel<256, true>, grid, block, stream, p);
   else
     return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MergeParams m;
   m.o_parts = p.ws_o;
@@ -639,14 +639,13 @@ hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t str
 hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream) {
   dim3 grid(p.R, d / 32), block(256);
   if (d == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, stream, p);
+    return launch_kernel(merge_kernel<128>, grid, block, stream, p);
   else if (d == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, stream, p);
+    return launch_kernel(merge_kernel<64>, grid, block, stream, p);
   else if (d == 256)
-    hipLaunchKernelGGL(merge_kernel<256>, grid, block, 0, stream, p);
+    return launch_kernel(merge_kernel<256>, grid, block, stream, p);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -248,7 +248,7 @@ fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* l
   if (!aligned16(o_parts) || !aligned16(o) || !aligned4(lse) || (lse_out && !aligned4(lse_out)))
     return FA_ERR_ALIGN;
   fa::MergeParams m;
-  m.o_parts = o_parts; m.lse = lse; m.o = o; m.lse_out = lse_out; m.lens = nullptr;
+  m.o_parts = o_parts; m.lse = lse; m.o = o; m.lse_out = lse_out; m.lens = nullptr; m.tps_dev = nullptr;
   m.R = R; m.S = S; m.Hq = 1; m.tps = 1; m.max_len = 0; m.out_bf16 = out_bf16 ? 1 : 0;
   return from_hip(fa::launch_merge(m, d, (hipStream_t)stream));
 }

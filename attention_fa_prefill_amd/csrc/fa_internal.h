@@ -18,6 +18,16 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// Enqueues kernel k (which takes one parameter block by value) and returns the
+// status of this launch alone. The runtime's pending "last error" is neither
+// read nor cleared, so an error the caller left behind is not reported as a
+// failure of this call, and stays the caller's to collect.
+template <typename P>
+inline hipError_t launch_kernel(void (*k)(P), dim3 grid, dim3 block, hipStream_t stream, const P& p) {
+  void* args[] = {const_cast<P*>(&p)};
+  return hipLaunchKernel(reinterpret_cast<const void*>(k), grid, block, args, 0, stream);
+}
+
 // ---------------------------------------------------------------- prefill
 struct PrefillParams {
   const void* q;

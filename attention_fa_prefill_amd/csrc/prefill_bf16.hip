@@ -648,14 +648,13 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream
   dim3 grid(cache ? (unsigned)(kXcds * ((groups + kXcds - 1) / kXcds) * per_group) : (unsigned)(p.nP * p.Hq * p.B));
   dim3 block(512);
   if (d == 128 && !cache)
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, stream, p);
+    return launch_kernel(prefill_bf16_kernel<128, false>, grid, block, stream, p);
   else if (d == 64 && !cache)
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, stream, p);
+    return launch_kernel(prefill_bf16_kernel<64, false>, grid, block, stream, p);
   else if (d == 128)
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, stream, p);
+    return launch_kernel(prefill_bf16_kernel<128, true>, grid, block, stream, p);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, stream, p);
-  return hipGetLastError();
+    return launch_kernel(prefill_bf16_kernel<64, true>, grid, block, stream, p);
 }
 
 }  // namespace fa

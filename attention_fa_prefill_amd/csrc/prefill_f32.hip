@@ -388,31 +388,29 @@ hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream)
   if (d <= 128 && (long)p.nT * p.Hq * p.B >= 128) {
     const dim3 grid(p.nT * p.Hq * p.B), block(256);
     if (d == 128)
-      hipLaunchKernelGGL(prefill_f32_mfma_kernel<128>, grid, block, 0, stream, p);
+      return launch_kernel(prefill_f32_mfma_kernel<128>, grid, block, stream, p);
     else if (d == 64)
-      hipLaunchKernelGGL(prefill_f32_mfma_kernel<64>, grid, block, 0, stream, p);
+      return launch_kernel(prefill_f32_mfma_kernel<64>, grid, block, stream, p);
     else if (d == 96)
-      hipLaunchKernelGGL(prefill_f32_mfma_kernel<96>, grid, block, 0, stream, p);
+      return launch_kernel(prefill_f32_mfma_kernel<96>, grid, block, stream, p);
     else if (d == 32)
-      hipLaunchKernelGGL(prefill_f32_mfma_kernel<32>, grid, block, 0, stream, p);
+      return launch_kernel(prefill_f32_mfma_kernel<32>, grid, block, stream, p);
     else
       return hipErrorInvalidValue;
-    return hipGetLastError();
   }
   dim3 grid((p.Sq + kRowsPerWG - 1) / kRowsPerWG, p.Hq, p.B), block(256);
   if (d == 128)
-    hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, stream, p);
+    return launch_kernel(prefill_f32_kernel<128>, grid, block, stream, p);
   else if (d == 64)
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, stream, p);
+    return launch_kernel(prefill_f32_kernel<64>, grid, block, stream, p);
   else if (d == 32)
-    hipLaunchKernelGGL(prefill_f32_kernel<32>, grid, block, 0, stream, p);
+    return launch_kernel(prefill_f32_kernel<32>, grid, block, stream, p);
   else if (d == 96)
-    hipLaunchKernelGGL(prefill_f32_kernel<96>, grid, block, 0, stream, p);
+    return launch_kernel(prefill_f32_kernel<96>, grid, block, stream, p);
   else if (d == 256)
-    hipLaunchKernelGGL(prefill_f32_kernel<256>, grid, block, 0, stream, p);
+    return launch_kernel(prefill_f32_kernel<256>, grid, block, stream, p);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -584,29 +584,26 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
     // 8 XCDs, longest sequences first; d = 256: the plain grid)
     const dim3 grid_c(kXcdsHd * ((p.B * p.Hkv + kXcdsHd - 1) / kXcdsHd) * (p.Hq / p.Hkv) * p.nT);
     if (d == 32)
-      hipLaunchKernelGGL((prefill_hd_kernel<32, true>), grid_c, block, 0, stream, p);
+      return launch_kernel(prefill_hd_kernel<32, true>, grid_c, block, stream, p);
     else if (d == 96)
-      hipLaunchKernelGGL((prefill_hd_kernel<96, true>), grid_c, block, 0, stream, p);
+      return launch_kernel(prefill_hd_kernel<96, true>, grid_c, block, stream, p);
     else if (d == 256)
-      hipLaunchKernelGGL((prefill_hd_kernel<256, true>), grid, block, 0, stream, p);
+      return launch_kernel(prefill_hd_kernel<256, true>, grid, block, stream, p);
     else
       return hipErrorInvalidValue;
-    return hipGetLastError();
   }
   // d = 256 grids of fewer than two rounds of 128-row tiles (one work-group
   // per CU) take the key-split kernel, whose 64-row tiles balance the CUs
   if (d == 32)
-    hipLaunchKernelGGL((prefill_hd_kernel<32, false>), grid, block, 0, stream, p);
+    return launch_kernel(prefill_hd_kernel<32, false>, grid, block, stream, p);
   else if (d == 96)
-    hipLaunchKernelGGL((prefill_hd_kernel<96, false>), grid, block, 0, stream, p);
+    return launch_kernel(prefill_hd_kernel<96, false>, grid, block, stream, p);
   else if (d == 256 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
-    hipLaunchKernelGGL(prefill_hd_ks_kernel<256>, dim3(((p.Sq + kTileKs - 1) / kTileKs) * p.Hq * p.B), block, 0,
-                       stream, p);
+    return launch_kernel(prefill_hd_ks_kernel<256>, dim3(((p.Sq + kTileKs - 1) / kTileKs) * p.Hq * p.B), block, stream, p);
   else if (d == 256)
-    hipLaunchKernelGGL((prefill_hd_kernel<256, false>), grid, block, 0, stream, p);
+    return launch_kernel(prefill_hd_kernel<256, false>, grid, block, stream, p);
   else
     return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -44,8 +44,12 @@
  *     its code and enqueues nothing. Device-resident integers (seqlens,
  *     block_table) are not read on the host; kernels clamp seqlens to
  *     [0, max_kv_len].
- *   - A launch error returns FA_ERR_HIP. Faults inside a kernel surface, as with
- *     any HIP work, at the caller's next synchronisation.
+ *   - A launch error returns FA_ERR_HIP. Only the status of this call's own
+ *     launches is reported: an error left pending by earlier runtime calls is
+ *     neither reported nor cleared (the library never calls hipGetLastError).
+ *     fa_decode and fa_decode_fp8 launch two kernels; if the second launch
+ *     fails, the first has been enqueued. Faults inside a kernel surface, as
+ *     with any HIP work, at the caller's next synchronisation.
  *   - The library keeps no mutable global state and is re-entrant; calls on
  *     different streams that share a workspace race.
  */

@@ -343,3 +343,41 @@ def as_fp8(case: DecodeCase, k_scale: float = 0.35, v_scale: float = 0.6, seed: 
     vc[case.vcache == BF16_NAN] = FP8_NAN
     return DecodeCase(case.name + "_fp8", case.B, case.Hq, case.Hkv, case.d, case.max_kv_len, case.scale,
                       case.seqlens.copy(), case.q, kc, vc, case.block_table, True, float(k_scale), float(v_scale))
+
+
+# Every finite OCP FP8 E4M3 code: all 256 but the two NaN codes 0x7F and 0xFF.
+E4M3_FINITE = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+
+
+def e4m3_codes_by_exponent(lo: int, hi: int) -> np.ndarray:
+    """The finite E4M3 codes whose biased exponent field (bits 6..3) is in
+    [lo, hi], both signs: field 0 holds the zeros and the subnormals, field 15
+    the largest binade (up to 448)."""
+    e = (E4M3_FINITE >> 3) & 0xF
+    return E4M3_FINITE[(e >= lo) & (e <= hi)]
+
+
+def fp8_every_code(case: DecodeCase, codes: np.ndarray, k_scale: float, v_scale: float, seed: int) -> DecodeCase:
+    """The same contiguous decode case (q, lengths) over an FP8 E4M3 cache whose
+    codes are drawn uniformly from ``codes``; every one of ``codes`` is also
+    placed, in a random order, among the first valid tokens of sequence 0 of
+    both K and V, so each appears where it is read. Slots past each length hold
+    the NaN code."""
+    assert not case.paged
+    codes = np.asarray(codes, dtype=np.uint8)
+    B, L, Hkv, d = case.kcache.shape
+    per_tok = Hkv * d
+    ntok = -(-len(codes) // per_tok)
+    assert int(case.seqlens[0]) >= ntok, "sequence 0 must hold one copy of every code"
+    out = []
+    for stream in (6, 7):
+        g = rng(seed, stream)
+        c = codes[g.integers(0, len(codes), size=case.kcache.shape)]
+        first = c[0, :ntok].reshape(-1)
+        first[: len(codes)] = g.permutation(codes)
+        c[0, :ntok] = first.reshape(ntok, Hkv, d)
+        for b in range(B):
+            c[b, max(0, min(int(case.seqlens[b]), L)):] = FP8_NAN
+        out.append(c)
+    return DecodeCase(case.name + "_fp8codes", case.B, case.Hq, case.Hkv, case.d, case.max_kv_len, case.scale,
+                      case.seqlens.copy(), case.q, out[0], out[1], None, True, float(k_scale), float(v_scale))
