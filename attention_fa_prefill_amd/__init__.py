@@ -23,7 +23,7 @@ FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
 EXPORTS = ("fa_status_string", "fa_version", "fa_prefill", "fa_prefill_f32", "fa_prefill_cache", "fa_decode_split_tokens",
-           "fa_decode_workspace_bytes", "fa_decode", "fa_decode_fp8", "fa_merge_lse")
+           "fa_decode_workspace_bytes", "fa_decode", "fa_decode_fp8", "fa_merge_lse", "fa_decode_noalloc")
 
 _lib = None
 
@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.fa_decode_fp8.restype = ci
         L.fa_merge_lse.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, vp]
         L.fa_merge_lse.restype = ci
+        L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp]
+        L.fa_decode_noalloc.restype = ci
         _lib = L
     return _lib
 
@@ -230,8 +232,19 @@ def decode_fp8(q, kcache, vcache, seqlens, *, k_scale: float, v_scale: float, bl
                    tokens_per_split, o, workspace, stream)
 
 
+def decode_noalloc(q, kcache, vcache, seqlens, o, *, block_table=None, max_kv_len: int | None = None,
+                   scale: float | None = None, tokens_per_split: int = 0, stream=None):
+    """decode without a workspace (``fa_decode_noalloc``): the split partials
+    live in the library's 16 MiB device array, so the call allocates nothing
+    (the caller passes o). Calls that may overlap on one GPU race."""
+    if o is None:
+        raise ValueError("decode_noalloc writes into a caller's o")
+    return _decode(q, kcache, vcache, seqlens, None, block_table, max_kv_len, scale, tokens_per_split, o, None,
+                   stream, noalloc=True)
+
+
 def _decode(q, kcache, vcache, seqlens, fp8_scales, block_table, max_kv_len, scale, tokens_per_split, o, workspace,
-            stream):
+            stream, noalloc=False):
     torch = _torch()
     if fp8_scales is None:
         if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
@@ -254,6 +267,11 @@ def _decode(q, kcache, vcache, seqlens, fp8_scales, block_table, max_kv_len, sca
         scale = 1.0 / math.sqrt(d)
     if o is None:
         o = torch.empty_like(q)
+    if noalloc:
+        check(lib().fa_decode_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(block_table), _ptr(seqlens), _ptr(o),
+                                      B, Hq, Hkv, d, mkl, page, int(tokens_per_split), float(scale),
+                                      _stream_handle(q, stream)))
+        return o
     need = decode_workspace_bytes(B, Hq, Hkv, d, mkl, tokens_per_split)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)

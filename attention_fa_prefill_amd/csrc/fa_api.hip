@@ -171,12 +171,42 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, 
 
 namespace {
 
+// Device scratch of fa_decode_noalloc: the split partials, their lse and the
+// split-size word of one call, in place of a caller's workspace. Each GPU the
+// library runs on holds its own copy for the life of the process. Host code
+// never uses the array's name as an address (on the host it is only a stand-in
+// for the symbol): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and is kept below.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device); nullptr and the runtime's status if it cannot be found.
+void* scratch_ptr(hipError_t* err) {
+  int dev = -1;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  *err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || !p) return nullptr;
+  scratch_addr[dev].store(p, std::memory_order_release);
+  return p;
+}
+
 // fa_decode and fa_decode_fp8: the same checks and plan; fp8 caches carry a
 // positive finite scale per tensor.
 fa_status decode_common(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
                         const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
                         int tokens_per_split, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, bool use_scratch = false) {
   if (!q || !kcache || !vcache || !seqlens || !o) return FA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_kv_len <= 0) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
@@ -194,6 +224,14 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   if ((long)B * nsplit_l * Hkv * hchunks > (long)INT32_MAX) return FA_ERR_SHAPE;
   if (!block_table && (size_t)B * (size_t)max_kv_len > (size_t)INT32_MAX) return FA_ERR_SHAPE;
   const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_kv_len, tps);
+  if (use_scratch) {
+    // the allocation-free variant: the device scratch array, within its size
+    if (need > kScratchBytes) return FA_ERR_WORKSPACE;
+    hipError_t e;
+    workspace = scratch_ptr(&e);
+    if (!workspace) return FA_ERR_HIP;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_ALIGN;
 
@@ -251,6 +289,13 @@ fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* l
   m.o_parts = o_parts; m.lse = lse; m.o = o; m.lse_out = lse_out; m.lens = nullptr; m.tps_dev = nullptr;
   m.R = R; m.S = S; m.Hq = 1; m.tps = 1; m.max_len = 0; m.out_bf16 = out_bf16 ? 1 : 0;
   return from_hip(fa::launch_merge(m, d, (hipStream_t)stream));
+}
+
+fa_status fa_decode_noalloc(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                            const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len,
+                            int page_size, int tokens_per_split, float scale, void* stream) {
+  return decode_common(q, kcache, vcache, block_table, seqlens, o, B, Hq, Hkv, d, max_kv_len, page_size,
+                       tokens_per_split, scale, false, 1.0f, 1.0f, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

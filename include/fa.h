@@ -253,6 +253,32 @@ fa_status fa_decode_fp8(const void* q, const void* kcache, const void* vcache,
 fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* lse_out,
                        int R, int S, int d, int out_bf16, void* stream);
 
+/*
+ * fa_decode_noalloc - fa_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc. It takes no workspace. The split partials live in a
+ * device array inside the library (16 MiB, one per GPU, held until the process
+ * ends); the call itself allocates, frees and copies nothing.
+ *
+ *   Arguments, layouts, results and every status of fa_decode (bf16 cache),
+ *   without workspace and workspace_bytes.
+ *   FA_ERR_WORKSPACE: the sizes need more than 16 MiB of partials, i.e.
+ *     fa_decode_workspace_bytes(B, Hq, Hkv, d, max_kv_len, tokens_per_split)
+ *     > 16777216 (for example B * Hq * ceil(max_kv_len / split) > 31,000 rows
+ *     at d = 128).
+ *   FA_ERR_HIP: the array's device address could not be obtained.
+ *
+ * The first call on a device looks up the array's address on that device; make
+ * it outside graph capture. All calls on one GPU share its array, which keeps
+ * the last call's contents (nothing in it needs clearing): calls that can
+ * overlap on one GPU (different streams, or replays of several captured
+ * graphs without ordering) race and must be serialised by the caller.
+ */
+fa_status fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* block_table, const int32_t* seqlens, void* o,
+                            int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
+                            int tokens_per_split, float scale, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
