@@ -18,6 +18,8 @@ Also reported on the same JSON line:
     each call timed alone after a 1 GiB read that evicts the 256 MB
     last-level cache (a read leaves no dirty lines behind);
   - us/call at B=1 for the fp32 single-head prefill and the bf16 prefill;
+  - launch modes for the fp32 single-head prefill and the long-context decode:
+    eager isolated, eager back-to-back and HIP-graph replay us/call;
   - ceilings: a plain streaming-read kernel's GB/s and an MFMA-loop kernel's
     bf16 TFLOP/s on the same GPU, the practical limits next to the peaks;
   - cpu_baseline: the fp64 oracle on the full prefill workload, host cores,
@@ -448,6 +450,90 @@ def main():
             case.name: {"us_per_call_p50": result["prefill_us_per_call_p50"]},
             "decode_long_b1h16x2kv256kd128": {"us_per_call_p50": long["us_per_call_p50"]},
         }
+
+        # ------------------------------------------------------------------ launch modes (C1 and C5)
+        # The same call issued three ways, all with inputs resident and caches
+        # warm: eager and isolated (an event pair around each call), eager and
+        # back-to-back (N calls between one event pair), and replayed from a HIP
+        # graph that holds N back-to-back calls (the FlashRT summary's capture-
+        # once, replay-per-token mechanism), plus a one-call graph replayed in
+        # isolation.
+        c5 = workloads.decode_long_256k()
+        q5, k5, v5 = bf16(c5.q), bf16(c5.kcache), bf16(c5.vcache)
+        lens5, bt5 = i32(c5.seqlens), i32(c5.block_table)
+        o5 = torch.empty_like(q5)
+        need5 = fa.decode_workspace_bytes(c5.B, c5.Hq, c5.Hkv, c5.d, c5.max_kv_len, 0)
+        ws5 = torch.empty(need5, dtype=torch.uint8, device=dev)
+
+        def c5call(st_handle):
+            st = L.fa_decode(ctypes.c_void_p(q5.data_ptr()), ctypes.c_void_p(k5.data_ptr()),
+                             ctypes.c_void_p(v5.data_ptr()), ctypes.c_void_p(bt5.data_ptr()),
+                             ctypes.c_void_p(lens5.data_ptr()), ctypes.c_void_p(o5.data_ptr()), c5.B, c5.Hq, c5.Hkv,
+                             c5.d, c5.max_kv_len, 16, 0, c5.scale, ctypes.c_void_p(ws5.data_ptr()), need5, st_handle)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+
+        def c1call_on(st_handle):
+            st = L.fa_prefill_f32(*a1[:-1], st_handle)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+
+        def launch_modes(call, n=20, reps=100):
+            cur = lambda: ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)  # noqa: E731
+            iso = timed_calls(lambda: call(ctypes_stream), reps, evict=False)
+            for _ in range(n):
+                call(ctypes_stream)
+            torch.cuda.synchronize()
+            b2b = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    call(ctypes_stream)
+                e1.record(stream)
+                e1.synchronize()
+                b2b.append(e0.elapsed_time(e1) * 1e3 / reps)
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):  # warm-up on a side stream before capture
+                call(cur())
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g_n, g_1 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_n):
+                for _ in range(n):
+                    call(cur())
+            with torch.cuda.graph(g_1):
+                call(cur())
+            torch.cuda.synchronize()
+            for _ in range(3):
+                g_n.replay()
+            torch.cuda.synchronize()
+            rep_n = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps // n):
+                    g_n.replay()
+                e1.record(stream)
+                e1.synchronize()
+                rep_n.append(e0.elapsed_time(e1) * 1e3 / (n * (reps // n)))
+            rep_1 = timed_calls(lambda: g_1.replay(), reps, evict=False)
+            del g_n, g_1
+            return {"eager_isolated_us_p50": round(statistics.median(iso), 2),
+                    "eager_back_to_back_us_per_call": round(statistics.median(b2b), 2),
+                    "graph_replay_back_to_back_us_per_call": round(statistics.median(rep_n), 2),
+                    "graph_replay_one_call_isolated_us_p50": round(statistics.median(rep_1), 2),
+                    "graph_calls_per_replay": n}
+
+        result["launch_modes"] = {
+            c1.name: launch_modes(c1call_on),
+            c5.name: launch_modes(c5call),
+            "note": "inputs resident, caches warm; back-to-back figures are the mean over 100 calls (median of 5 "
+                    "runs); the graph holds 20 calls and is replayed 5 times per run; isolated figures are the "
+                    "median of 100 calls, each between its own event pair"}
+        del q5, k5, v5, lens5, bt5, o5, ws5
+        torch.cuda.empty_cache()
 
         # ------------------------------------------------------------------ practical ceilings
         C = ctypes.CDLL(os.path.join(ROOT, "attention_fa_prefill_amd", "libfa_ceiling.so"))
