@@ -115,7 +115,7 @@ fa_status fa_prefill(const void* q, const void* k, const void* v, void* o, int B
   fa_status st = check_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, d, scale, causal);
   if (st != FA_OK) return st;
   fa::PrefillParams p = make_prefill(q, k, v, o, B, Hq, Hkv, Sq, Skv, scale, causal);
-  if (d == 64 || d == 128) return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+  if (d == 64 || d == 96 || d == 128) return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
   p.cus = resident_split_groups() / 2;
   return from_hip(fa::launch_prefill_hd(p, d, (hipStream_t)stream));
 }
@@ -141,7 +141,7 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
   p.bt = block_table;
   p.max_len = max_kv_len;
   p.pps = (max_kv_len + 15) / 16;
-  if (d == 64 || d == 128) return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+  if (d == 64 || d == 96 || d == 128) return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
   return from_hip(fa::launch_prefill_hd(p, d, (hipStream_t)stream));
 }
 

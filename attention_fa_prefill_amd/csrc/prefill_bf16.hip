@@ -49,6 +49,11 @@
 // The K loads of block k+1 are issued one at a time between the MFMAs of
 // M(k), the V loads of block k at the start of V(k); the wave in its MFMA
 // slot runs at raised issue priority (s_setprio 1).
+//
+// Head dims 64, 96 and 128. An LDS row holds a power-of-two number of 16-byte
+// chunks so that the XOR swizzles stay inside it: d = 96 rows (12 chunks) are
+// padded to 16, and the direct-to-LDS lanes that land on padding chunks get
+// an out-of-range buffer offset, so they read nothing and write zeros.
 #include "fa_internal.h"
 
 namespace fa {
@@ -62,11 +67,15 @@ constexpr int kXcds = 8;
 constexpr int kRankMaxB = 512;  // sequences ordered by length in every work-group up to this batch     // MI355X: 8 accelerator complex dies, one L2 each
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
+constexpr uint32_t kPadOff = 0x80000000u;  // a buffer offset past any block: the load returns zeros
+
 template <int D>
 struct Cfg {
   static constexpr int CH = D / 8;               // 16-byte chunks per K/V row
-  static constexpr int ELEMS = kBN * D;          // bf16 elements per K or V block
-  static constexpr int NI = kBN * CH / 64 / 4;   // direct-to-LDS loads per wave per block
+  static constexpr int RP = D == 96 ? 16 : CH;   // chunks per LDS row (padded to a power of two)
+  static constexpr int RB = RP * 16;             // bytes per LDS row
+  static constexpr int ELEMS = kBN * RP * 8;     // bf16 elements per K or V block in LDS
+  static constexpr int NI = kBN * RP / 64 / 4;   // direct-to-LDS loads per wave per block
   static constexpr int KS = D / 16;              // k-steps of S^T = K . Q^T
   static constexpr int DB = D / 32;              // 32-row d blocks of O^T
   static constexpr int XO = 64 * DB * 16;        // floats of one wave's O^T in the exchange
@@ -74,14 +83,15 @@ struct Cfg {
 
 // LDS swizzles (16-byte chunk index XOR a function of the row).
 // K (and staged Q) rows are read 16 bytes per lane for 16 consecutive rows at
-// one chunk: XOR with row mod CH spreads them over all banks.
+// one chunk: XOR with row mod RP spreads them over all banks.
 template <int D>
-__device__ __forceinline__ int swz_k(int row) { return row & (Cfg<D>::CH - 1); }
+__device__ __forceinline__ int swz_k(int row) { return row & (Cfg<D>::RP - 1); }
 // V is read by transpose reads: each 16-lane group touches 4 consecutive rows x
-// 32 bytes. XOR with 2*(row%4) (D=64) / 4*(row%4) (D=128) places those 4 rows
-// in different bank windows and keeps each 32-byte pair of chunks together.
+// 32 bytes. XOR with 2*(row%4) (8-chunk rows) / 4*(row%4) (16-chunk rows)
+// places those 4 rows in different bank windows and keeps each 32-byte pair of
+// chunks together.
 template <int D>
-__device__ __forceinline__ int swz_v(int row) { return (D == 128 ? 4 : 2) * (row & 3); }
+__device__ __forceinline__ int swz_v(int row) { return (Cfg<D>::RP >= 16 ? 4 : 2) * (row & 3); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -130,7 +140,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[2 * C::ELEMS];
   __shared__ __attribute__((aligned(1024))) __bf16 sK1[2 * C::ELEMS];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[2 * C::ELEMS];
-  __shared__ __attribute__((aligned(1024))) __bf16 sQ[kBM * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 sQ[kBM * C::RP * 8];
 
   const int tid = threadIdx.x;
   // The wave index is uniform across the wave: keep it (and everything derived
@@ -216,20 +226,22 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   const __bf16* qbh = (const __bf16*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
 
   // Per-lane byte offsets (inside a 64-key block) of this lane's direct-to-LDS
-  // loads: LDS chunk P of the block holds logical chunk (P % CH) ^ swz(row) of
-  // row P / CH.
+  // loads: LDS chunk P of the block holds logical chunk (P % RP) ^ swz(row) of
+  // row P / RP; a padding chunk (logical >= CH, D = 96) gets an out-of-range
+  // offset and is written as zeros.
   // (CACHE: wave wg's loads of a block cover exactly its 16 rows 16 wg ..
   // 16 wg + 15, one page, and rows are rowstride bytes apart.)
-  static_assert(64 * C::NI / C::CH == 16, "one page of rows per wave and block");
+  static_assert(64 * C::NI / C::RP == 16, "one page of rows per wave and block");
   const uint32_t rowstride = CACHE ? (uint32_t)p.Hkv * D * 2u : (uint32_t)D * 2u;
   uint32_t koff[C::NI], voff[C::NI];
 #pragma unroll
   for (int ii = 0; ii < C::NI; ++ii) {
     const int P = 64 * (wg * C::NI + ii) + lane;
-    const int row = P / C::CH, pc = P % C::CH;
+    const int row = P / C::RP, pc = P % C::RP;
+    const int lk = pc ^ swz_k<D>(row), lv = pc ^ swz_v<D>(row);
     const uint32_t rbase = (uint32_t)(CACHE ? (row & 15) : row) * rowstride;
-    koff[ii] = rbase + (uint32_t)((pc ^ swz_k<D>(row)) << 4);
-    voff[ii] = rbase + (uint32_t)((pc ^ swz_v<D>(row)) << 4);
+    koff[ii] = lk < C::CH ? rbase + (uint32_t)(lk << 4) : kPadOff;
+    voff[ii] = lv < C::CH ? rbase + (uint32_t)(lv << 4) : kPadOff;
   }
   // CACHE: buffer resource over this wave's page of block j of the K (or V)
   // cache; its record count ends after the last key that exists, so rows past
@@ -307,7 +319,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   // flip. No second read of Q from memory.
   auto share_q = [&]() __attribute__((always_inline)) {
     const int row = wg * 32 + ln;
-    char* base = (char*)sQ + row * (D * 2);
+    char* base = (char*)sQ + row * C::RB;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       uint4 x = __builtin_bit_cast(uint4, qreg[ks]);
@@ -317,7 +329,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
   };
   auto load_q_lds = [&]() __attribute__((always_inline)) {
     const int row = wg * 32 + ln;
-    const char* base = (const char*)sQ + row * (D * 2);
+    const char* base = (const char*)sQ + row * C::RB;
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
       uint4 x = *(const uint4*)(base + (((2 * ks + hl) ^ swz_k<D>(row)) << 4));
@@ -345,7 +357,7 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     }
   };
 
-  const int kr0 = ln * (D * 2), kr1 = (32 + ln) * (D * 2);
+  const int kr0 = ln * C::RB, kr1 = (32 + ln) * C::RB;
   const int sw0 = swz_k<D>(ln), sw1 = swz_k<D>(32 + ln);
   auto kread = [&](const char* kbase, int kr, int sw, int ks) __attribute__((always_inline)) {
     return *(const bf16x8*)(kbase + kr + (((2 * ks + hl) ^ sw) << 4));
@@ -357,8 +369,8 @@ __global__ void __launch_bounds__(512) prefill_bf16_kernel(PrefillParams p) {
     const int row1 = 32 * sub + 16 * s + 4 * hl + (jj >> 2);
     const int row2 = row1 + 8;
     const int colb = (32 * db + 16 * dh + 4 * (jj & 3)) * 2;
-    const char* a1 = vbase + row1 * (D * 2) + (((colb >> 4) ^ swz_v<D>(row1)) << 4) + (colb & 15);
-    const char* a2 = vbase + row2 * (D * 2) + (((colb >> 4) ^ swz_v<D>(row2)) << 4) + (colb & 15);
+    const char* a1 = vbase + row1 * C::RB + (((colb >> 4) ^ swz_v<D>(row1)) << 4) + (colb & 15);
+    const char* a2 = vbase + row2 * C::RB + (((colb >> 4) ^ swz_v<D>(row2)) << 4) + (colb & 15);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -649,12 +661,18 @@ hipError_t launch_prefill_bf16(const PrefillParams& p, int d, hipStream_t stream
   dim3 block(512);
   if (d == 128 && !cache)
     return launch_kernel(prefill_bf16_kernel<128, false>, grid, block, stream, p);
+  else if (d == 96 && !cache)
+    return launch_kernel(prefill_bf16_kernel<96, false>, grid, block, stream, p);
   else if (d == 64 && !cache)
     return launch_kernel(prefill_bf16_kernel<64, false>, grid, block, stream, p);
   else if (d == 128)
     return launch_kernel(prefill_bf16_kernel<128, true>, grid, block, stream, p);
-  else
+  else if (d == 96)
+    return launch_kernel(prefill_bf16_kernel<96, true>, grid, block, stream, p);
+  else if (d == 64)
     return launch_kernel(prefill_bf16_kernel<64, true>, grid, block, stream, p);
+  else
+    return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -1,5 +1,5 @@
 // bf16 prefill for the head dims the ping-pong kernel does not provide
-// (d = 32, 96, 256): causal or non-causal MQA/GQA attention with an online
+// (d = 32, 256): causal or non-causal MQA/GQA attention with an online
 // softmax, fp32 accumulation, bf16 MFMA for both products.
 //
 // It computes the tiled attention of the "Real-time inference optimisation"
@@ -17,13 +17,13 @@
 //     K read from LDS with ds_read_b128 and V^T with ds_read_b64_tr_b16;
 //   - K/V blocks of 64 keys come in by direct-to-LDS loads
 //     (buffer_load_dwordx4 ... lds), double-buffered, one barrier per block;
-//   - LDS rows are padded to a power-of-two number of 16-byte chunks (8 for
-//     d = 32, 16 for d = 96) so the XOR swizzles stay inside the row; the
+//   - LDS rows are padded to a power-of-two number of at least 8 16-byte
+//     chunks (8 for d = 32) so the XOR swizzles stay inside the row; the
 //     padding chunks are filled with zeros by out-of-range buffer loads;
 //   - d = 256 needs O^T (128 registers) and Q^T (64) per wave, so it runs one
 //     wave per SIMD with up to 512 registers and 128 KB of LDS per work-group;
-//     d = 32 and 96 run two or more work-groups per CU, whose waves overlap
-//     each other's MFMA and softmax phases;
+//     d = 32 runs two or more work-groups per CU, whose waves overlap each
+//     other's MFMA and softmax phases;
 //   - d = 256 grids of fewer than two rounds of 128-row tiles (one work-group
 //     per CU) run prefill_hd_ks_kernel instead: 64-row tiles whose keys are
 //     split between two wave pairs (below).
@@ -580,13 +580,11 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
     // chunked prefill over a KV cache: the one-group kernel, one work-group
     // per (query tile, head, sequence), padded to whole rounds of (sequence,
     // kv head) groups on the 8 XCDs
-    // (d = 32, 96: padded to whole rounds of (sequence, kv head) groups on the
+    // (d = 32: padded to whole rounds of (sequence, kv head) groups on the
     // 8 XCDs, longest sequences first; d = 256: the plain grid)
     const dim3 grid_c(kXcdsHd * ((p.B * p.Hkv + kXcdsHd - 1) / kXcdsHd) * (p.Hq / p.Hkv) * p.nT);
     if (d == 32)
       return launch_kernel(prefill_hd_kernel<32, true>, grid_c, block, stream, p);
-    else if (d == 96)
-      return launch_kernel(prefill_hd_kernel<96, true>, grid_c, block, stream, p);
     else if (d == 256)
       return launch_kernel(prefill_hd_kernel<256, true>, grid, block, stream, p);
     else
@@ -596,8 +594,6 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
   // per CU) take the key-split kernel, whose 64-row tiles balance the CUs
   if (d == 32)
     return launch_kernel(prefill_hd_kernel<32, false>, grid, block, stream, p);
-  else if (d == 96)
-    return launch_kernel(prefill_hd_kernel<96, false>, grid, block, stream, p);
   else if (d == 256 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
     return launch_kernel(prefill_hd_ks_kernel<256>, dim3(((p.Sq + kTileKs - 1) / kTileKs) * p.Hq * p.B), block, stream, p);
   else if (d == 256)

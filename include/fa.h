@@ -93,9 +93,10 @@ int fa_version(void);
  *
  * QK^T and PV run on bf16 MFMA with fp32 accumulation; the probabilities are
  * rounded to bf16 before the PV product; o is rounded to bf16 (RNE).
- * d = 64 and 128 run on the two-group ping-pong kernel; d = 32, 96 and 256
- * on a one-group kernel (one 128-row query tile per work-group, 64-key K/V
- * blocks double-buffered in LDS; d = 256 at one wave per SIMD for its 128
+ * d = 64, 96 and 128 run on the two-group ping-pong kernel (d = 96 with its
+ * LDS rows padded to 16 chunks of 16 bytes); d = 32 and 256 on a one-group
+ * kernel (one 128-row query tile per work-group, 64-key K/V blocks
+ * double-buffered in LDS; d = 256 at one wave per SIMD for its 128
  * accumulator registers).
  * o must not alias q, k or v.
  */
@@ -135,12 +136,12 @@ fa_status fa_prefill_f32(const void* q, const void* k, const void* v, void* o,
  *   scale, d, stream, errors : as for fa_prefill (d = 32, 64, 96, 128 or
  *                 256), plus FA_ERR_NULL for a NULL seqlens and
  *                 FA_ERR_UNSUPPORTED for a page size other than 16.
- * The same kernels as fa_prefill compute it. At d = 64 and 128 the ping-pong
- * kernel takes one query tile per work-group (the sequences' tiles ordered
- * by cached length, longest first), so with a cache holding exactly
- * fa_prefill's K and V the two agree to rounding; at d = 32, 96 and 256 the
- * one-group kernel runs as for fa_prefill (at d = 32 and 96 with the same
- * bits; d = 256 may differ from fa_prefill's key-split kernel by rounding).
+ * The same kernels as fa_prefill compute it. At d = 64, 96 and 128 the
+ * ping-pong kernel takes one query tile per work-group (the sequences' tiles
+ * ordered by cached length, longest first), so with a cache holding exactly
+ * fa_prefill's K and V the two agree to rounding; at d = 32 and 256 the
+ * one-group kernel runs as for fa_prefill (at d = 32 with the same bits;
+ * d = 256 may differ from fa_prefill's key-split kernel by rounding).
  * For the same seqlens the paged and contiguous caches give bitwise equal
  * results.
  */
