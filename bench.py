@@ -25,7 +25,7 @@ Also reported on the same JSON line:
   - cpu_baseline: the fp64 oracle on the full prefill workload, host cores,
     repeated for about 10 s.
 Only one GPU is used; --gpus above 1 exits with a message.
---prefill-only and --decode-only run one leg (for profiler passes).
+--prefill-only, --decode-only and --only LEG run one leg (for profiler passes).
 """
 from __future__ import annotations
 
@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the decode leg and print its results (not the headline line)")
     ap.add_argument("--decode-reps", type=int, default=50)
+    ap.add_argument("--only", choices=["prefill_cache", "head_dims", "f32_large"],
+                    help="run only this leg and print its results (not the headline line); for profiler passes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device-to-device copies (HBM counter calibration)")
     args = ap.parse_args()
@@ -233,8 +235,120 @@ def main():
             torch.cuda.empty_cache()
         return dec
 
+    def leg_prefill_cache():
+        """chunked prefill over the paged cache of the chunk workload"""
+        # chunked prefill over a paged KV cache (fa_prefill_cache): back-to-back
+        # calls with the cache resident, the same timing as the headline
+        pc = workloads.prefill_cache_chunk512()
+        pq, pk, pv = bf16(pc.q), bf16(pc.kcache), bf16(pc.vcache)
+        plens, pbt = i32(pc.seqlens), i32(pc.block_table)
+        po = torch.empty_like(pq)
+        pargs = (ctypes.c_void_p(pq.data_ptr()), ctypes.c_void_p(pk.data_ptr()), ctypes.c_void_p(pv.data_ptr()),
+                 ctypes.c_void_p(pbt.data_ptr()), ctypes.c_void_p(plens.data_ptr()), ctypes.c_void_p(po.data_ptr()),
+                 pc.B, pc.Hq, pc.Hkv, pc.Sq, pc.d, pc.max_kv_len, 16, pc.scale, 1, ctypes_stream)
+
+        def pcall():
+            st = L.fa_prefill_cache(*pargs)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+        for _ in range(200):
+            pcall()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(100):
+            pcall()
+        ev1.record(stream)
+        ev1.synchronize()
+        pc_us = ev0.elapsed_time(ev1) * 1e3 / 100
+        pc_flop = sum(prefill_flops(1, pc.Hq, pc.Sq, int(L_), pc.d, True) for L_ in pc.seqlens)
+        return {
+            "workload": pc.name, "us_per_call_mean": round(pc_us, 2),
+            "TFLOP_per_s": round(pc_flop / (pc_us * 1e-6) / 1e12, 1),
+            "frac_of_bf16_peak": round(pc_flop / (pc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "algorithmic_flop_per_call": pc_flop, "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "Sq": pc.Sq, "d": pc.d,
+            "cached_lengths": [int(x) for x in pc.seqlens], "paged": True, "causal": True,
+            "note": "chunk of Sq new queries per sequence over its paged cache (chunk included); 100 back-to-back calls"}
+
+    def leg_head_dims():
+        """head dims 256 and 96"""
+        # head dims 256 and 96: back-to-back calls, as above
+        n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+        def hd_kernel_name(hc):
+            # d = 256 grids under two rounds of 128-row tiles take the key-split kernel
+            tiles = -(-hc.Sq // 128) * hc.Hq * hc.B
+            if hc.d == 96:
+                return "prefill_bf16_kernel<96, false>"
+            return "prefill_hd_ks_kernel<256>" if hc.d == 256 and tiles < 2 * n_cus else f"prefill_hd_kernel<{hc.d}>"
+        hd = {}
+        for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96()):
+            hq_, hk_, hv_ = bf16(hc.q), bf16(hc.k), bf16(hc.v)
+            ho = torch.empty_like(hq_)
+            hargs = (ctypes.c_void_p(hq_.data_ptr()), ctypes.c_void_p(hk_.data_ptr()), ctypes.c_void_p(hv_.data_ptr()),
+                     ctypes.c_void_p(ho.data_ptr()), hc.B, hc.Hq, hc.Hkv, hc.Sq, hc.Skv, hc.d, hc.scale, 1,
+                     ctypes_stream)
+
+            def hcall(hargs=hargs):
+                st = L.fa_prefill(*hargs)
+                if st != 0:
+                    raise RuntimeError(fa.status_string(st))
+            for _ in range(200):
+                hcall()
+            torch.cuda.synchronize()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(100):
+                hcall()
+            ev1.record(stream)
+            ev1.synchronize()
+            h_us = ev0.elapsed_time(ev1) * 1e3 / 100
+            h_flop = prefill_flops(hc.B, hc.Hq, hc.Sq, hc.Skv, hc.d, True)
+            hd[hc.name] = {"us_per_call_mean": round(h_us, 2), "TFLOP_per_s": round(h_flop / (h_us * 1e-6) / 1e12, 1),
+                           "frac_of_bf16_peak": round(h_flop / (h_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "algorithmic_flop_per_call": h_flop, "B": hc.B, "Hq": hc.Hq, "Hkv": hc.Hkv, "Sq": hc.Sq,
+                           "d": hc.d, "causal": True, "kernel": hd_kernel_name(hc)}
+            del hq_, hk_, hv_, ho
+        return hd
+
+    def leg_f32_large():
+        """fp32 prefill at the C2 shape"""
+        # fp32 prefill at the C2 shape (the matrix-core fp32 kernel), timed like
+        # the head-dim legs, against the fp32 matrix peak
+        fc = workloads.prefill_case(1, 32, 8, 2048, 2048, 128, True, "f32", seed=1002, scale=128 ** -0.5,
+                                    name="prefill_f32_gqa_b1h32x8s2048d128")
+        fq, fk, fv = (torch.from_numpy(x).to(dev) for x in (fc.q, fc.k, fc.v))
+        fo = torch.empty_like(fq)
+        fargs = (ctypes.c_void_p(fq.data_ptr()), ctypes.c_void_p(fk.data_ptr()), ctypes.c_void_p(fv.data_ptr()),
+                 ctypes.c_void_p(fo.data_ptr()), 1, 32, 8, 2048, 2048, 128, fc.scale, 1, ctypes_stream)
+
+        def fcall():
+            st = L.fa_prefill_f32(*fargs)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+        for _ in range(30):
+            fcall()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(30):
+            fcall()
+        ev1.record(stream)
+        ev1.synchronize()
+        f_us = ev0.elapsed_time(ev1) * 1e3 / 30
+        f_flop = prefill_flops(1, 32, 2048, 2048, 128, True)
+        return {
+            "workload": fc.name, "us_per_call_mean": round(f_us, 2),
+            "TFLOP_per_s": round(f_flop / (f_us * 1e-6) / 1e12, 2),
+            "frac_of_fp32_peak": round(f_flop / (f_us * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
+            "kernel": "prefill_f32_mfma_kernel<128>", "note": "30 back-to-back calls after 30 warm-up calls"}
+
     if args.decode_only:
         print(json.dumps({"decode": decode_leg()}), flush=True)
+        return
+    if args.only:
+        leg = {"prefill_cache": leg_prefill_cache, "head_dims": leg_head_dims, "f32_large": leg_f32_large}[args.only]
+        print(json.dumps({args.only: leg()}), flush=True)
         return
 
     # ------------------------------------------------------------------ headline: GQA causal prefill
@@ -319,107 +433,9 @@ def main():
             "workload": "decode_long_b1h16x2kv256kd128_fp8",
             "note": "FP8 E4M3 cache (1 byte per element); split + merge kernels per call, caches evicted before each call"}
 
-        # chunked prefill over a paged KV cache (fa_prefill_cache): back-to-back
-        # calls with the cache resident, the same timing as the headline
-        pc = workloads.prefill_cache_chunk512()
-        pq, pk, pv = bf16(pc.q), bf16(pc.kcache), bf16(pc.vcache)
-        plens, pbt = i32(pc.seqlens), i32(pc.block_table)
-        po = torch.empty_like(pq)
-        pargs = (ctypes.c_void_p(pq.data_ptr()), ctypes.c_void_p(pk.data_ptr()), ctypes.c_void_p(pv.data_ptr()),
-                 ctypes.c_void_p(pbt.data_ptr()), ctypes.c_void_p(plens.data_ptr()), ctypes.c_void_p(po.data_ptr()),
-                 pc.B, pc.Hq, pc.Hkv, pc.Sq, pc.d, pc.max_kv_len, 16, pc.scale, 1, ctypes_stream)
-
-        def pcall():
-            st = L.fa_prefill_cache(*pargs)
-            if st != 0:
-                raise RuntimeError(fa.status_string(st))
-        for _ in range(200):
-            pcall()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(100):
-            pcall()
-        ev1.record(stream)
-        ev1.synchronize()
-        pc_us = ev0.elapsed_time(ev1) * 1e3 / 100
-        pc_flop = sum(prefill_flops(1, pc.Hq, pc.Sq, int(L_), pc.d, True) for L_ in pc.seqlens)
-        result["prefill_cache"] = {
-            "workload": pc.name, "us_per_call_mean": round(pc_us, 2),
-            "TFLOP_per_s": round(pc_flop / (pc_us * 1e-6) / 1e12, 1),
-            "frac_of_bf16_peak": round(pc_flop / (pc_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "algorithmic_flop_per_call": pc_flop, "B": pc.B, "Hq": pc.Hq, "Hkv": pc.Hkv, "Sq": pc.Sq, "d": pc.d,
-            "cached_lengths": [int(x) for x in pc.seqlens], "paged": True, "causal": True,
-            "note": "chunk of Sq new queries per sequence over its paged cache (chunk included); 100 back-to-back calls"}
-        del pq, pk, pv, plens, pbt, po
-
-        # head dims 256 and 96 (their own kernel): back-to-back calls, as above
-        n_cus = torch.cuda.get_device_properties(0).multi_processor_count
-
-        def hd_kernel_name(hc):
-            # d = 256 grids under two rounds of 128-row tiles take the key-split kernel
-            tiles = -(-hc.Sq // 128) * hc.Hq * hc.B
-            return "prefill_hd_ks_kernel<256>" if hc.d == 256 and tiles < 2 * n_cus else f"prefill_hd_kernel<{hc.d}>"
-        hd = {}
-        for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96()):
-            hq_, hk_, hv_ = bf16(hc.q), bf16(hc.k), bf16(hc.v)
-            ho = torch.empty_like(hq_)
-            hargs = (ctypes.c_void_p(hq_.data_ptr()), ctypes.c_void_p(hk_.data_ptr()), ctypes.c_void_p(hv_.data_ptr()),
-                     ctypes.c_void_p(ho.data_ptr()), hc.B, hc.Hq, hc.Hkv, hc.Sq, hc.Skv, hc.d, hc.scale, 1,
-                     ctypes_stream)
-
-            def hcall(hargs=hargs):
-                st = L.fa_prefill(*hargs)
-                if st != 0:
-                    raise RuntimeError(fa.status_string(st))
-            for _ in range(200):
-                hcall()
-            torch.cuda.synchronize()
-            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            ev0.record(stream)
-            for _ in range(100):
-                hcall()
-            ev1.record(stream)
-            ev1.synchronize()
-            h_us = ev0.elapsed_time(ev1) * 1e3 / 100
-            h_flop = prefill_flops(hc.B, hc.Hq, hc.Sq, hc.Skv, hc.d, True)
-            hd[hc.name] = {"us_per_call_mean": round(h_us, 2), "TFLOP_per_s": round(h_flop / (h_us * 1e-6) / 1e12, 1),
-                           "frac_of_bf16_peak": round(h_flop / (h_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
-                           "algorithmic_flop_per_call": h_flop, "B": hc.B, "Hq": hc.Hq, "Hkv": hc.Hkv, "Sq": hc.Sq,
-                           "d": hc.d, "causal": True, "kernel": hd_kernel_name(hc)}
-            del hq_, hk_, hv_, ho
-        result["prefill_head_dims"] = hd
-
-        # fp32 prefill at the C2 shape (the matrix-core fp32 kernel), timed like
-        # the head-dim legs, against the fp32 matrix peak
-        fc = workloads.prefill_case(1, 32, 8, 2048, 2048, 128, True, "f32", seed=1002, scale=128 ** -0.5,
-                                    name="prefill_f32_gqa_b1h32x8s2048d128")
-        fq, fk, fv = (torch.from_numpy(x).to(dev) for x in (fc.q, fc.k, fc.v))
-        fo = torch.empty_like(fq)
-        fargs = (ctypes.c_void_p(fq.data_ptr()), ctypes.c_void_p(fk.data_ptr()), ctypes.c_void_p(fv.data_ptr()),
-                 ctypes.c_void_p(fo.data_ptr()), 1, 32, 8, 2048, 2048, 128, fc.scale, 1, ctypes_stream)
-
-        def fcall():
-            st = L.fa_prefill_f32(*fargs)
-            if st != 0:
-                raise RuntimeError(fa.status_string(st))
-        for _ in range(30):
-            fcall()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        for _ in range(30):
-            fcall()
-        ev1.record(stream)
-        ev1.synchronize()
-        f_us = ev0.elapsed_time(ev1) * 1e3 / 30
-        f_flop = prefill_flops(1, 32, 2048, 2048, 128, True)
-        result["prefill_f32_large"] = {
-            "workload": fc.name, "us_per_call_mean": round(f_us, 2),
-            "TFLOP_per_s": round(f_flop / (f_us * 1e-6) / 1e12, 2),
-            "frac_of_fp32_peak": round(f_flop / (f_us * 1e-6) / 1e12 / PEAK_FP32_TFLOPS, 4),
-            "kernel": "prefill_f32_mfma_kernel<128>", "note": "30 back-to-back calls after 30 warm-up calls"}
-        del fq, fk, fv, fo
+        result["prefill_cache"] = leg_prefill_cache()
+        result["prefill_head_dims"] = leg_head_dims()
+        result["prefill_f32_large"] = leg_f32_large()
 
         # decode at head dim 256 (one split work-group per CU), bf16 and FP8
         # caches, timed like the decode legs above
