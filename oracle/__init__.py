@@ -204,6 +204,27 @@ def decode_fp8(q, kcodes, vcodes, seqlens, scale: float, k_scale: float, v_scale
                   lib=lib)
 
 
+def int8_to_f64(codes) -> np.ndarray:
+    """Signed 8-bit integers (two's complement) to fp64, from the definition:
+    a byte c = 0..255 holds c when c < 128 and c - 256 otherwise, so the
+    range is -128..127. This is the element of the INT8 KV cache of the
+    FasterTransformer walkthrough (section 3.3: an 8-bit KV cache that halves
+    the bytes a decode step reads), with one scale per tensor."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
+
+
+def decode_int8(q, kcodes, vcodes, seqlens, scale: float, k_scale: float, v_scale: float, block_table=None,
+                page_size: int = 16, max_kv_len=None, lib: str | None = None):
+    """decode over an INT8 cache with one scale per tensor: the cache is
+    dequantised (K = k_scale * code, V = v_scale * code) and the same
+    definition applied in fp64. Returns (o [B, Hq, d], lse [B, Hq])."""
+    kc = int8_to_f64(kcodes) * float(k_scale)
+    vc = int8_to_f64(vcodes) * float(v_scale)
+    return decode(q, kc, vc, seqlens, scale, block_table=block_table, page_size=page_size, max_kv_len=max_kv_len,
+                  lib=lib)
+
+
 def merge(o_parts, lse_parts, lib: str | None = None):
     """Log-sum-exp merge. o_parts [R, S, d] (normalised parts), lse_parts [R, S].
     Returns (o [R, d], lse [R])."""

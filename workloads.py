@@ -148,8 +148,9 @@ class DecodeCase:
     vcache: np.ndarray = field(repr=False)
     block_table: np.ndarray | None = field(default=None, repr=False)  # int32 [B, ceil(max_kv_len/16)]
     fp8: bool = False        # kcache / vcache hold uint8 OCP FP8 E4M3 codes
-    k_scale: float = 1.0     # per-tensor scales of an fp8 cache
+    k_scale: float = 1.0     # per-tensor scales of an fp8 or int8 cache
     v_scale: float = 1.0
+    int8: bool = False       # kcache / vcache hold signed 8-bit integer codes (as uint8 bytes)
 
     @property
     def paged(self) -> bool:
@@ -256,7 +257,7 @@ def paged_from_contiguous(case: DecodeCase, seed: int = 99) -> DecodeCase:
     kp[bt.reshape(-1)] = case.kcache.reshape(B * pps, PAGE, case.Hkv, case.d)
     vp[bt.reshape(-1)] = case.vcache.reshape(B * pps, PAGE, case.Hkv, case.d)
     return DecodeCase(case.name + "_paged", case.B, case.Hq, case.Hkv, case.d, L, case.scale,
-                      case.seqlens.copy(), case.q, kp, vp, bt, case.fp8, case.k_scale, case.v_scale)
+                      case.seqlens.copy(), case.q, kp, vp, bt, case.fp8, case.k_scale, case.v_scale, case.int8)
 
 
 # --------------------------------------------------------------------------- chunked prefill over a KV cache
@@ -381,3 +382,28 @@ def fp8_every_code(case: DecodeCase, codes: np.ndarray, k_scale: float, v_scale:
         out.append(c)
     return DecodeCase(case.name + "_fp8codes", case.B, case.Hq, case.Hkv, case.d, case.max_kv_len, case.scale,
                       case.seqlens.copy(), case.q, out[0], out[1], None, True, float(k_scale), float(v_scale))
+
+
+# --------------------------------------------------------------------------- int8 KV cache
+
+INT8_POISON = 0x7F  # the largest code (127): garbage of the largest magnitude in slots past a length
+
+
+def int8_codes(seed: int, stream: int, shape) -> np.ndarray:
+    """Random signed 8-bit codes, stored as uint8 bytes (two's complement):
+    uniform over all 256 values, -128..127."""
+    return rng(seed, stream).integers(0, 256, size=int(np.prod(shape)), dtype=np.uint8).reshape(shape)
+
+
+def as_int8(case: DecodeCase, k_scale: float = 1.0 / 64, v_scale: float = 0.02, seed: int | None = None) -> DecodeCase:
+    """The same decode case (q, lengths, block table) over an INT8 cache of
+    random codes with per-tensor scales; slots that hold NaN in the bf16 cache
+    (poisoned tails and pages) hold the code 127."""
+    sd = (zlib.crc32(case.name.encode()) % 100000) if seed is None else seed
+    kc = int8_codes(sd, 10, case.kcache.shape)
+    vc = int8_codes(sd, 11, case.vcache.shape)
+    kc[case.kcache == BF16_NAN] = INT8_POISON
+    vc[case.vcache == BF16_NAN] = INT8_POISON
+    return DecodeCase(case.name + "_int8", case.B, case.Hq, case.Hkv, case.d, case.max_kv_len, case.scale,
+                      case.seqlens.copy(), case.q, kc, vc, case.block_table, False, float(k_scale), float(v_scale),
+                      True)
