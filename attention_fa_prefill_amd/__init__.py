@@ -23,7 +23,8 @@ FA_OK = 0
 STATUS_NAMES = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED", 4: "FA_ERR_ALIGN",
                 5: "FA_ERR_WORKSPACE", 6: "FA_ERR_HIP", 7: "FA_ERR_ARG"}
 EXPORTS = ("fa_status_string", "fa_version", "fa_prefill", "fa_prefill_f32", "fa_prefill_cache", "fa_decode_split_tokens",
-           "fa_decode_workspace_bytes", "fa_decode", "fa_decode_fp8", "fa_merge_lse", "fa_decode_noalloc")
+           "fa_decode_workspace_bytes", "fa_decode", "fa_decode_fp8", "fa_merge_lse", "fa_decode_noalloc",
+           "fa_decode_int8")
 
 _lib = None
 
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.fa_decode.restype = ci
         L.fa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, cf, cf, vp, sz, vp]
         L.fa_decode_fp8.restype = ci
+        L.fa_decode_int8.argtypes = L.fa_decode_fp8.argtypes
+        L.fa_decode_int8.restype = ci
         L.fa_merge_lse.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, vp]
         L.fa_merge_lse.restype = ci
         L.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, ci, cf, vp]
@@ -232,6 +235,16 @@ def decode_fp8(q, kcache, vcache, seqlens, *, k_scale: float, v_scale: float, bl
                    tokens_per_split, o, workspace, stream)
 
 
+def decode_int8(q, kcache, vcache, seqlens, *, k_scale: float, v_scale: float, block_table=None,
+                max_kv_len: int | None = None, scale: float | None = None, tokens_per_split: int = 0, o=None,
+                workspace=None, stream=None):
+    """decode over an INT8 cache: kcache, vcache hold signed 8-bit codes
+    (int8 or uint8 tensors holding the two's-complement bytes, same layouts as
+    decode); K = k_scale * code, V = v_scale * code. q and o bf16."""
+    return _decode(q, kcache, vcache, seqlens, (float(k_scale), float(v_scale)), block_table, max_kv_len, scale,
+                   tokens_per_split, o, workspace, stream, fmt="int8")
+
+
 def decode_noalloc(q, kcache, vcache, seqlens, o, *, block_table=None, max_kv_len: int | None = None,
                    scale: float | None = None, tokens_per_split: int = 0, stream=None):
     """decode without a workspace (``fa_decode_noalloc``): the split partials
@@ -244,11 +257,15 @@ def decode_noalloc(q, kcache, vcache, seqlens, o, *, block_table=None, max_kv_le
 
 
 def _decode(q, kcache, vcache, seqlens, fp8_scales, block_table, max_kv_len, scale, tokens_per_split, o, workspace,
-            stream, noalloc=False):
+            stream, noalloc=False, fmt="fp8"):
     torch = _torch()
     if fp8_scales is None:
         if q.dtype != torch.bfloat16 or kcache.dtype != torch.bfloat16 or vcache.dtype != torch.bfloat16:
             raise ValueError("decode takes bfloat16 q and caches")
+    elif fmt == "int8":
+        if q.dtype != torch.bfloat16 or kcache.dtype not in (torch.int8, torch.uint8) or \
+                vcache.dtype not in (torch.int8, torch.uint8):
+            raise ValueError("decode_int8 takes a bfloat16 q and int8 / uint8 caches")
     else:
         byte_types = (torch.uint8,) + ((torch.float8_e4m3fn,) if hasattr(torch, "float8_e4m3fn") else ())
         if q.dtype != torch.bfloat16 or kcache.dtype not in byte_types or vcache.dtype not in byte_types:
@@ -280,6 +297,8 @@ def _decode(q, kcache, vcache, seqlens, fp8_scales, block_table, max_kv_len, sca
     tail = (_ptr(workspace), workspace.numel() * workspace.element_size(), _stream_handle(q, stream))
     if fp8_scales is None:
         check(lib().fa_decode(*common, *tail))
+    elif fmt == "int8":
+        check(lib().fa_decode_int8(*common, *fp8_scales, *tail))
     else:
         check(lib().fa_decode_fp8(*common, *fp8_scales, *tail))
     return o

@@ -103,6 +103,16 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 x) {
   return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// 8 signed 8-bit integers in two's complement (byte i of x = element i) -> 8
+// bf16, exactly (every integer in -128..127 is a bf16 value); the per-tensor
+// scale is applied elsewhere.
+__device__ __forceinline__ bf16x8 int8x8_to_bf16(u32x2 x) {
+  auto e = [](uint32_t w, int k) __attribute__((always_inline)) { return (float)((int)(w << (24 - 8 * k)) >> 24); };
+  const uint4 r = make_uint4(pack2(e(x.x, 0), e(x.x, 1)), pack2(e(x.x, 2), e(x.x, 3)),
+                             pack2(e(x.y, 0), e(x.y, 1)), pack2(e(x.y, 2), e(x.y, 3)));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave, on DPP: shifts by 1, 2,
 // 4 and 8 lanes inside each row of 16 (lanes shifted in from outside the row
 // add 0), then the last lane of row 0 (of row 2) is added to row 1 (to row 3)
@@ -117,13 +127,21 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
   return x;
 }
 
-// F8: the cache holds OCP FP8 E4M3 codes (one byte per element) with one
-// scale per tensor: K = p.ks * code, V = p.vs * code. p.ks is folded into the
-// softmax factor c by the host and p.vs is applied to each split's output;
-// K and V are widened to bf16 exactly, so the arithmetic is that of the bf16
-// cache on the dequantised values.
-template <int D, bool F8>
+// F8: the cache holds one byte per element, OCP FP8 E4M3 codes (I8 false) or
+// signed 8-bit integers (I8 true), with one scale per tensor: K = p.ks * code,
+// V = p.vs * code. p.ks is folded into the softmax factor c by the host and
+// p.vs is applied to each split's output; K and V are widened to bf16
+// exactly, so the arithmetic is that of the bf16 cache on the dequantised
+// values.
+template <int D, bool F8, bool I8>
 __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
+  static_assert(F8 || !I8, "the int8 cache is a one-byte cache");
+  auto byte8_to_bf16 = [](u32x2 x) __attribute__((always_inline)) {
+    if constexpr (I8)
+      return int8x8_to_bf16(x);
+    else
+      return fp8x8_to_bf16(x);
+  };
   constexpr int ES = F8 ? 1 : 2;     // bytes per cached element
   constexpr int KS = D / 32;         // k-steps of S^T = K . Q^T (16x16x32)
   constexpr int DB = D / 16;         // 16-dim blocks of O^T
@@ -317,7 +335,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   };
   auto k_operand = [&](const KReg& x) __attribute__((always_inline)) {
     if constexpr (F8)
-      return fp8x8_to_bf16(x);
+      return byte8_to_bf16(x);
     else
       return __builtin_bit_cast(bf16x8, x);
   };
@@ -405,7 +423,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
       for (int db = 0; db < DB; ++db) {
         const char* a8 = vslot + trow * D + ((db ^ swz_v8<D>(trow)) << 4) + 8 * (lane & 1);
         const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)a8);
-        O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(__builtin_bit_cast(u32x2, v8)), pop, O[db], 0, 0, 0);
+        O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(byte8_to_bf16(__builtin_bit_cast(u32x2, v8)), pop, O[db], 0, 0, 0);
       }
       return;
     }
@@ -602,21 +620,27 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream) {
+hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stream) {
   dim3 grid(p.B * p.nsplit * p.Hkv * p.hchunks), block(256);
   hipError_t e;
-  if (d == 128 && !fp8)
-    e = launch_kernel(decode_split_kernel<128, false>, grid, block, stream, p);
-  else if (d == 64 && !fp8)
-    e = launch_kernel(decode_split_kernel<64, false>, grid, block, stream, p);
-  else if (d == 256 && !fp8)
-    e = launch_kernel(decode_split_kernel<256, false>, grid, block, stream, p);
-  else if (d == 128)
-    e = launch_kernel(decode_split_kernel<128, true>, grid, block, stream, p);
-  else if (d == 64)
-    e = launch_kernel(decode_split_kernel<64, true>, grid, block, stream, p);
-  else if (d == 256)
-    e = launch_kernel(decode_split_kernel<256, true>, grid, block, stream, p);
+  if (fmt == kCacheBf16 && d == 128)
+    e = launch_kernel(decode_split_kernel<128, false, false>, grid, block, stream, p);
+  else if (fmt == kCacheBf16 && d == 64)
+    e = launch_kernel(decode_split_kernel<64, false, false>, grid, block, stream, p);
+  else if (fmt == kCacheBf16 && d == 256)
+    e = launch_kernel(decode_split_kernel<256, false, false>, grid, block, stream, p);
+  else if (fmt == kCacheFp8 && d == 128)
+    e = launch_kernel(decode_split_kernel<128, true, false>, grid, block, stream, p);
+  else if (fmt == kCacheFp8 && d == 64)
+    e = launch_kernel(decode_split_kernel<64, true, false>, grid, block, stream, p);
+  else if (fmt == kCacheFp8 && d == 256)
+    e = launch_kernel(decode_split_kernel<256, true, false>, grid, block, stream, p);
+  else if (fmt == kCacheInt8 && d == 128)
+    e = launch_kernel(decode_split_kernel<128, true, true>, grid, block, stream, p);
+  else if (fmt == kCacheInt8 && d == 64)
+    e = launch_kernel(decode_split_kernel<64, true, true>, grid, block, stream, p);
+  else if (fmt == kCacheInt8 && d == 256)
+    e = launch_kernel(decode_split_kernel<256, true, true>, grid, block, stream, p);
   else
     return hipErrorInvalidValue;
   if (e != hipSuccess) return e;

@@ -201,11 +201,11 @@ void* scratch_ptr(hipError_t* err) {
   return p;
 }
 
-// fa_decode and fa_decode_fp8: the same checks and plan; fp8 caches carry a
-// positive finite scale per tensor.
+// fa_decode, fa_decode_fp8 and fa_decode_int8: the same checks and plan; the
+// one-byte caches carry a positive finite scale per tensor.
 fa_status decode_common(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
                         const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
-                        int tokens_per_split, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
+                        int tokens_per_split, float scale, int fmt, float k_scale, float v_scale, void* workspace,
                         size_t workspace_bytes, void* stream, bool use_scratch = false) {
   if (!q || !kcache || !vcache || !seqlens || !o) return FA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_kv_len <= 0) return FA_ERR_SHAPE;
@@ -215,7 +215,8 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   const int tps = fa_decode_split_tokens(B, Hq, Hkv, max_kv_len, tokens_per_split);
   if (tps <= 0) return FA_ERR_ARG;
   if (!isfinite(scale)) return FA_ERR_ARG;
-  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return FA_ERR_ARG;
+  const bool bytes = fmt != fa::kCacheBf16;
+  if (bytes && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(o)) return FA_ERR_ALIGN;
   if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
   const int G = Hq / Hkv;
@@ -248,15 +249,15 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   // (d = 256: one split work-group per CU, its registers and LDS allow no second)
   p.cap = d == 256 ? resident_split_groups() / 2 : resident_split_groups();
   // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0;
-  // an fp8 K scale multiplies every score, so it joins c
-  p.c = fmaxf(fabsf(scale) * (fp8 ? k_scale : 1.0f) * fa::kLog2e, 1e-30f);
-  p.vs = fp8 ? v_scale : 1.0f;
+  // a one-byte cache's K scale multiplies every score, so it joins c
+  p.c = fmaxf(fabsf(scale) * (bytes ? k_scale : 1.0f) * fa::kLog2e, 1e-30f);
+  p.vs = bytes ? v_scale : 1.0f;
   p.neg = scale < 0.f ? 1 : 0;
   const size_t rows = (size_t)B * Hq * p.nsplit;
   p.ws_o = (float*)workspace;
   p.ws_lse = (float*)((char*)workspace + round_up(rows * d * sizeof(float), 256));
   p.ws_t = (int*)((char*)p.ws_lse + round_up(rows * sizeof(float), 256));
-  return from_hip(fa::launch_decode(p, d, fp8, (hipStream_t)stream));
+  return from_hip(fa::launch_decode(p, d, fmt, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -267,7 +268,7 @@ fa_status fa_decode(const void* q, const void* kcache, const void* vcache, const
                     const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
                     int tokens_per_split, float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return decode_common(q, kcache, vcache, block_table, seqlens, o, B, Hq, Hkv, d, max_kv_len, page_size,
-                       tokens_per_split, scale, false, 1.0f, 1.0f, workspace, workspace_bytes, stream);
+                       tokens_per_split, scale, fa::kCacheBf16, 1.0f, 1.0f, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_decode_fp8(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
@@ -275,7 +276,15 @@ fa_status fa_decode_fp8(const void* q, const void* kcache, const void* vcache, c
                         int tokens_per_split, float scale, float k_scale, float v_scale, void* workspace,
                         size_t workspace_bytes, void* stream) {
   return decode_common(q, kcache, vcache, block_table, seqlens, o, B, Hq, Hkv, d, max_kv_len, page_size,
-                       tokens_per_split, scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
+                       tokens_per_split, scale, fa::kCacheFp8, k_scale, v_scale, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_decode_int8(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                         const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len, int page_size,
+                         int tokens_per_split, float scale, float k_scale, float v_scale, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  return decode_common(q, kcache, vcache, block_table, seqlens, o, B, Hq, Hkv, d, max_kv_len, page_size,
+                       tokens_per_split, scale, fa::kCacheInt8, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* lse_out, int R, int S, int d,
@@ -295,7 +304,7 @@ fa_status fa_decode_noalloc(const void* q, const void* kcache, const void* vcach
                             const int32_t* seqlens, void* o, int B, int Hq, int Hkv, int d, int max_kv_len,
                             int page_size, int tokens_per_split, float scale, void* stream) {
   return decode_common(q, kcache, vcache, block_table, seqlens, o, B, Hq, Hkv, d, max_kv_len, page_size,
-                       tokens_per_split, scale, false, 1.0f, 1.0f, nullptr, 0, stream, true);
+                       tokens_per_split, scale, fa::kCacheBf16, 1.0f, 1.0f, nullptr, 0, stream, true);
 }
 
 }  // extern "C"

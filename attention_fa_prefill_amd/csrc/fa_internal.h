@@ -65,8 +65,8 @@ struct DecodeParams {
   int B, Hq, Hkv, max_len, pages_per_seq, tps, nsplit;
   int G;               // query heads per kv head
   int hchunks;         // ceil(G / 16)
-  float c;             // |scale| * log2(e) (FP8 cache: times the K scale)
-  float vs;            // V scale (FP8 cache), 1 for bf16
+  float c;             // |scale| * log2(e) (one-byte cache: times the K scale)
+  float vs;            // V scale (one-byte cache), 1 for bf16
   int neg;
   int compact;         // number live splits densely (B small enough to scan per work-group)
   int adapt;           // compact and default split size: the kernel may enlarge tps
@@ -74,8 +74,10 @@ struct DecodeParams {
   int* ws_t;           // the split size the split kernel used (written by work-group 0)
 };
 
-// fp8: kc / vc hold OCP FP8 E4M3 codes (K = c-folded scale * code, V = vs * code)
-hipError_t launch_decode(const DecodeParams& p, int d, bool fp8, hipStream_t stream);
+// KV-cache element formats: bf16; one byte per element, OCP FP8 E4M3 codes or
+// signed 8-bit integers (K = c-folded scale * code, V = vs * code)
+constexpr int kCacheBf16 = 0, kCacheFp8 = 1, kCacheInt8 = 2;
+hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stream);
 
 struct MergeParams {
   const float* o_parts;  // [R, S, d]

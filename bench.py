@@ -14,7 +14,8 @@ Also reported on the same JSON line:
     HBM traffic from the committed rocprofv3 counter summary when it was taken
     on the current kernel source, else null;
   - decode: contiguous 32k (B=4), paged mixed lengths (B=8) and long-context
-    256k (B=1): us/call (both kernels) and algorithmic HBM GB/s against 8 TB/s,
+    256k (B=1), over bf16, FP8 E4M3 and int8 caches: us/call (both kernels)
+    and algorithmic HBM GB/s against 8 TB/s,
     each call timed alone after a 1 GiB read that evicts the 256 MB
     last-level cache (a read leaves no dirty lines behind);
   - us/call at B=1 for the fp32 single-head prefill and the bf16 prefill;
@@ -71,7 +72,7 @@ def decode_bytes(case):
     import numpy as np
 
     lens = np.clip(case.seqlens, 0, case.max_kv_len).astype(np.int64)
-    es = 1 if getattr(case, "fp8", False) else 2  # bytes per cached element (FP8 E4M3 or bf16)
+    es = 1 if (getattr(case, "fp8", False) or getattr(case, "int8", False)) else 2  # bytes per cached element
     b = es * 2 * case.Hkv * case.d * int(lens.sum()) + 2 * 2 * case.B * case.Hq * case.d + 4 * case.B
     if case.paged:
         b += 4 * int(((lens + 15) // 16).sum())
@@ -184,9 +185,10 @@ def main():
 
     def decode_leg(makers=(workloads.decode_contig_32k, workloads.decode_paged_mixed, workloads.decode_long_256k)):
         dec = {}
-        cases = [m() for m in makers] + [workloads.as_fp8(m()) for m in makers]
+        cases = ([m() for m in makers] + [workloads.as_fp8(m()) for m in makers] +
+                 [workloads.as_int8(m()) for m in makers])
         for dc in cases:
-            if dc.fp8:  # FP8 E4M3 codes, one byte per element
+            if dc.fp8 or dc.int8:  # FP8 E4M3 or int8 codes, one byte per element
                 dk = torch.from_numpy(np.ascontiguousarray(dc.kcache)).to(dev)
                 dv = torch.from_numpy(np.ascontiguousarray(dc.vcache)).to(dev)
                 dq = bf16(dc.q)
@@ -204,9 +206,11 @@ def main():
                      ctypes.c_void_p(od.data_ptr()), dc.B, dc.Hq, dc.Hkv, dc.d, dc.max_kv_len,
                      16 if dc.paged else 0, 0, dc.scale, ctypes.c_void_p(ws.data_ptr()), need, ctypes_stream)
 
-            def dcall(dargs=dargs, fp8=dc.fp8, ks=dc.k_scale, vs=dc.v_scale):
+            def dcall(dargs=dargs, fp8=dc.fp8, int8=dc.int8, ks=dc.k_scale, vs=dc.v_scale):
                 if fp8:
                     st = L.fa_decode_fp8(*dargs[:14], ks, vs, *dargs[14:])
+                elif int8:
+                    st = L.fa_decode_int8(*dargs[:14], ks, vs, *dargs[14:])
                 else:
                     st = L.fa_decode(*dargs)
                 if st != 0:
@@ -226,9 +230,9 @@ def main():
                             "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "d": dc.d, "tokens": dc.total_tokens(),
                             "paged": dc.paged, "tokens_per_split": tps,
                             "splits_per_kv_head": int(sum(-(-min(int(x), dc.max_kv_len) // tps) for x in dc.seqlens)),
-                            "kv_cache": "fp8_e4m3" if dc.fp8 else "bf16"}
-            if dc.fp8:
-                base = dec[dc.name[: -len("_fp8")]]
+                            "kv_cache": "fp8_e4m3" if dc.fp8 else ("int8" if dc.int8 else "bf16")}
+            if dc.fp8 or dc.int8:
+                base = dec[dc.name[: -len("_fp8" if dc.fp8 else "_int8")]]
                 dec[dc.name]["k_scale"], dec[dc.name]["v_scale"] = dc.k_scale, dc.v_scale
                 dec[dc.name]["speedup_vs_bf16_cache"] = round(base["us_per_call_p50"] / p50, 3)
             del dq, dk, dv, ws, od, lens, bt

@@ -93,14 +93,14 @@ def test_decode_rejects(kw, code):
     assert decode(**kw) == code
 
 
-def decode_fp8(ks=0.5, vs=0.5, **kw):
+def decode_fp8(ks=0.5, vs=0.5, fn="fa_decode_fp8", **kw):
     a = dict(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, page=16, tps=0, scale=0.1, ws=A,
              wsb=None)
     a.update(kw)
     if a["wsb"] is None:
         a["wsb"] = fa.decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["d"], a["L"], a["tps"]) if a["B"] > 0 else 0
-    return fa.lib().fa_decode_fp8(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["o"], a["B"], a["Hq"], a["Hkv"],
-                                  a["d"], a["L"], a["page"], a["tps"], a["scale"], ks, vs, a["ws"], a["wsb"], None)
+    return getattr(fa.lib(), fn)(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["o"], a["B"], a["Hq"], a["Hkv"],
+                                 a["d"], a["L"], a["page"], a["tps"], a["scale"], ks, vs, a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -109,9 +109,45 @@ def decode_fp8(ks=0.5, vs=0.5, **kw):
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(d=96), UNSUP), (dict(Hq=6, Hkv=4), SHAPE),
     (dict(tps=48), ARG), (dict(k=A + 8), ALIGN), (dict(wsb=16), WS),
 ])
-def test_decode_fp8_rejects(kw, code):
-    """The fp8 entry point checks what fa_decode checks, and its scales (finite, > 0)."""
-    assert decode_fp8(**kw) == code
+@pytest.mark.parametrize("fn", ["fa_decode_fp8", "fa_decode_int8"])
+def test_decode_byte_cache_rejects(fn, kw, code):
+    """The fp8 and int8 entry points check what fa_decode checks, and their
+    scales (finite, > 0)."""
+    assert decode_fp8(fn=fn, **kw) == code
+
+
+def noalloc(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, page=16, tps=0, scale=0.1):
+    return fa.lib().fa_decode_noalloc(q, k, v, bt, lens, o, B, Hq, Hkv, d, L, page, tps, scale, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(lens=None), NULL), (dict(B=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE),
+    (dict(d=96), UNSUP), (dict(bt=A, page=32), UNSUP), (dict(tps=48), ARG), (dict(scale=float("inf")), ARG),
+    (dict(k=A + 8), ALIGN),
+    # partials beyond the 16 MiB device array
+    (dict(B=64, Hq=32, Hkv=8, L=32768, tps=64), WS), (dict(B=2, Hq=64, Hkv=8, d=256, L=65536, tps=256), WS),
+])
+def test_decode_noalloc_rejects(kw, code):
+    """fa_decode_noalloc checks what fa_decode checks (without a workspace),
+    and rejects sizes whose partials do not fit its device array."""
+    assert noalloc(**kw) == code
+
+
+def test_decode_noalloc_limit_is_16_mib():
+    """Every size whose partials need more than 16 MiB is rejected on the host
+    (sizes that fit are not called here: they would launch)."""
+    lim = 16 << 20
+    over = 0
+    for B in (1, 2, 4, 8, 16, 32):
+        for L, tps in ((32768, 64), (65536, 128), (262144, 256), (16384, 32)):
+            need = fa.decode_workspace_bytes(B, 32, 8, 128, L, tps)
+            if need > lim:
+                assert noalloc(B=B, Hq=32, Hkv=8, L=L, tps=tps) == WS, (B, L, tps, need)
+                over += 1
+    assert over > 5
+    # the boundary: 16 MiB is 2^24 bytes; rows * (128 + 1) * 4 + rounding + 256 crosses it between these two
+    assert fa.decode_workspace_bytes(1, 32, 8, 128, 32 * 1016, 32) <= lim
+    assert noalloc(B=1, Hq=32, Hkv=8, L=32 * 1017, tps=32) == WS
 
 
 def test_decode_split_tokens():
