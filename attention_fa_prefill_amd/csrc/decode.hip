@@ -55,18 +55,27 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 // V staging swizzle: 16-byte chunk XOR 2*(row % 8) (D=128, 256) / 2*(row % 4) (D=64),
 // so the 4-row x 32-byte footprint of each transpose read hits distinct banks.
-template <int D>
-__device__ __forceinline__ int swz_v(int row) { return 2 * (row & (D >= 128 ? 7 : 3)); }
+// (CP: 16-byte chunks per LDS row of the stage, a power of two; rows of
+// d = 96 are padded to it)
+template <int CP>
+__device__ __forceinline__ int swz_v(int row) { return 2 * (row & (CP >= 16 ? 7 : CP / 2 - 1)); }
 // FP8 V staging swizzle. A transpose read of 8-bit elements (ds_read_b64_tr_b8)
 // by 16 lanes covers one 16-byte chunk of 8 rows: tokens 4cq..4cq+3 and
 // 16+4cq..16+4cq+3 of the step. XOR with a function of the row that differs
-// on those 8 rows (D=128, 256: 8 or 16 chunks per row) or, with the row's
-// parity, still separates them (D=64: 4 chunks per 64-byte row) places the 8
-// reads in distinct banks.
-template <int D>
+// on those 8 rows (8 or 16 chunks per row) or, with the row's parity, still
+// separates them (4 chunks per 64-byte row) places the 8 reads in distinct
+// banks.
+template <int CP>
 __device__ __forceinline__ int swz_v8(int row) {
-  return D >= 128 ? ((row & 3) | (((row >> 4) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 4) & 1) << 1));
+  return CP >= 8 ? ((row & 3) | (((row >> 4) & 1) << 2)) : (((row >> 1) & 1) | (((row >> 4) & 1) << 1));
 }
+
+constexpr int pow2_at_least(int x, int lo) {
+  int r = lo;
+  while (r < x) r *= 2;
+  return r;
+}
+constexpr uint32_t kPadOffset = 0x80000000u;  // a buffer offset past any page: the load returns zeros
 
 // Waits for this wave's vector-memory loads (direct-to-LDS included) until at
 // most N are outstanding. The memory clobber keeps LDS reads of a stage from
@@ -146,14 +155,22 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   constexpr int KS = D / 32;         // k-steps of S^T = K . Q^T (16x16x32)
   constexpr int DB = D / 16;         // 16-dim blocks of O^T
   constexpr int CH = D * ES / 16;    // 16-byte chunks per row
-  constexpr int RI = 64 / CH;        // V rows per direct-to-LDS load (bf16 D=128: 4; fp8: 8)
+  // LDS stage rows hold CP chunks, a power of two (so the XOR swizzles stay
+  // inside the row) and at least 4 (so a direct-to-LDS load stays inside one
+  // page of 16 rows): d = 96 rows and d = 32 FP8 rows are padded; the lanes
+  // that land on padding chunks load nothing and write zeros.
+  constexpr int CP = pow2_at_least(CH, 4);
+  constexpr int RB = CP * 16;        // bytes per LDS stage row
+  constexpr int RI = 64 / CP;        // V rows per direct-to-LDS load (bf16 D=128: 4; fp8: 8)
   constexpr int VDMA = kStep / RI;   // direct-to-LDS loads per step
   constexpr int NLD = 2 * KS + VDMA; // vector-memory instructions issued per step
   // Two V stages per wave (the step being used and the one in flight); an
   // FP8 step uses the first half of a stage. sV0 doubles as the exchange of
   // the 4 waves' states at the end.
-  __shared__ __attribute__((aligned(1024))) __bf16 sV0[4][kStep * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV1[4][kStep * D];
+  // (sized for bf16 rows: the exchange at the end needs 64 D bytes per wave)
+  constexpr int STG = kStep * pow2_at_least(D / 8, 4) * 8;
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[4][STG];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[4][STG];
   __shared__ float sM[4][64], sL[4][64];
   __shared__ int sRow0[kPageSlots];  // first cache row of each page of this split
 
@@ -344,11 +361,12 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   auto dma_v = [&](int st, __bf16* stage) __attribute__((always_inline)) {
 #pragma unroll
     for (int ii = 0; ii < VDMA; ++ii) {
-      const int r = ii * RI + lane / CH, pc = lane % CH;
+      const int r = ii * RI + lane / CP, pc = lane % CP;
       const int h = (ii * RI) / 16;  // page of this load (uniform)
       const __amdgpu_buffer_rsrc_t rs = page_rsrc(p.vc, 2 * st + h);
-      const int sw = F8 ? swz_v8<D>(r) : swz_v<D>(r);
-      const int voff = (int)((size_t)(r & 15) * rowstride) + ((pc ^ sw) << 4);
+      const int sw = F8 ? swz_v8<CP>(r) : swz_v<CP>(r);
+      const int lc = pc ^ sw;  // logical chunk of the row
+      const int voff = lc < CH ? (int)((size_t)(r & 15) * rowstride) + (lc << 4) : (int)kPadOffset;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + ii * 64 * 8), 16, voff, 0, 0, 0);
     }
   };
@@ -421,7 +439,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
     if constexpr (F8) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const char* a8 = vslot + trow * D + ((db ^ swz_v8<D>(trow)) << 4) + 8 * (lane & 1);
+        const char* a8 = vslot + trow * RB + ((db ^ swz_v8<CP>(trow)) << 4) + 8 * (lane & 1);
         const i32x2 v8 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)a8);
         O[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(byte8_to_bf16(__builtin_bit_cast(u32x2, v8)), pop, O[db], 0, 0, 0);
       }
@@ -430,8 +448,8 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const int colb = (16 * db + 4 * (y & 3)) * 2;
-      const char* a1 = vslot + row1 * (D * 2) + (((colb >> 4) ^ swz_v<D>(row1)) << 4) + (colb & 15);
-      const char* a2 = vslot + row2 * (D * 2) + (((colb >> 4) ^ swz_v<D>(row2)) << 4) + (colb & 15);
+      const char* a1 = vslot + row1 * RB + (((colb >> 4) ^ swz_v<CP>(row1)) << 4) + (colb & 15);
+      const char* a2 = vslot + row2 * RB + (((colb >> 4) ^ swz_v<CP>(row2)) << 4) + (colb & 15);
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
       const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -641,6 +659,18 @@ hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stre
     e = launch_kernel(decode_split_kernel<64, true, true>, grid, block, stream, p);
   else if (fmt == kCacheInt8 && d == 256)
     e = launch_kernel(decode_split_kernel<256, true, true>, grid, block, stream, p);
+  else if (fmt == kCacheBf16 && d == 96)
+    e = launch_kernel(decode_split_kernel<96, false, false>, grid, block, stream, p);
+  else if (fmt == kCacheBf16 && d == 32)
+    e = launch_kernel(decode_split_kernel<32, false, false>, grid, block, stream, p);
+  else if (fmt == kCacheFp8 && d == 96)
+    e = launch_kernel(decode_split_kernel<96, true, false>, grid, block, stream, p);
+  else if (fmt == kCacheFp8 && d == 32)
+    e = launch_kernel(decode_split_kernel<32, true, false>, grid, block, stream, p);
+  else if (fmt == kCacheInt8 && d == 96)
+    e = launch_kernel(decode_split_kernel<96, true, true>, grid, block, stream, p);
+  else if (fmt == kCacheInt8 && d == 32)
+    e = launch_kernel(decode_split_kernel<32, true, true>, grid, block, stream, p);
   else
     return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
@@ -668,6 +698,10 @@ hipError_t launch_merge(const MergeParams& p, int d, hipStream_t stream) {
     return launch_kernel(merge_kernel<64>, grid, block, stream, p);
   else if (d == 256)
     return launch_kernel(merge_kernel<256>, grid, block, stream, p);
+  else if (d == 96)
+    return launch_kernel(merge_kernel<96>, grid, block, stream, p);
+  else if (d == 32)
+    return launch_kernel(merge_kernel<32>, grid, block, stream, p);
   else
     return hipErrorInvalidValue;
 }

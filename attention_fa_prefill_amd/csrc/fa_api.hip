@@ -99,7 +99,7 @@ const char* fa_status_string(fa_status s) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid sizes (<= 0, Hq % Hkv != 0, causal with Sq > Skv, or too large)";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim or page_size not provided (prefill d = 32, 64, 96, 128, 256; decode 64, 128, 256; page_size 16)";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim or page_size not provided (d = 32, 64, 96, 128, 256; page_size 16)";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensor pointers must be 16-byte aligned";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime rejected a launch";
@@ -210,7 +210,7 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   if (!q || !kcache || !vcache || !seqlens || !o) return FA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || max_kv_len <= 0) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   if (block_table && page_size != 16) return FA_ERR_UNSUPPORTED;
   const int tps = fa_decode_split_tokens(B, Hq, Hkv, max_kv_len, tokens_per_split);
   if (tps <= 0) return FA_ERR_ARG;
@@ -291,7 +291,7 @@ fa_status fa_merge_lse(const float* o_parts, const float* lse, void* o, float* l
                        int out_bf16, void* stream) {
   if (!o_parts || !lse || !o) return FA_ERR_NULL;
   if (R <= 0 || S <= 0 || d <= 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
+  if (d != 32 && d != 64 && d != 96 && d != 128 && d != 256) return FA_ERR_UNSUPPORTED;
   if (!aligned16(o_parts) || !aligned16(o) || !aligned4(lse) || (lse_out && !aligned4(lse_out)))
     return FA_ERR_ALIGN;
   fa::MergeParams m;

@@ -82,8 +82,8 @@ def decode(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, p
     (dict(q=None), NULL), (dict(k=None), NULL), (dict(v=None), NULL), (dict(lens=None), NULL), (dict(o=None), NULL),
     (dict(B=0, wsb=1 << 20), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(L=0, wsb=1 << 20), SHAPE),
     (dict(Hkv=0), SHAPE),
-    (dict(d=80), UNSUP), (dict(d=96), UNSUP), (dict(d=512), UNSUP), (dict(bt=A, page=32), UNSUP),
-    (dict(bt=A, page=8), UNSUP),
+    (dict(d=80), UNSUP), (dict(d=48), UNSUP), (dict(d=16), UNSUP), (dict(d=512), UNSUP),
+    (dict(bt=A, page=32), UNSUP), (dict(bt=A, page=8), UNSUP),
     (dict(tps=48), ARG), (dict(tps=-32), ARG), (dict(tps=4096), ARG), (dict(scale=float("nan")), ARG),
     (dict(q=A + 2), ALIGN), (dict(k=A + 8), ALIGN), (dict(o=A + 4), ALIGN), (dict(lens=A + 2), ALIGN),
     (dict(bt=A + 1), ALIGN), (dict(ws=A + 8), ALIGN),
@@ -106,7 +106,7 @@ def decode_fp8(ks=0.5, vs=0.5, fn="fa_decode_fp8", **kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(ks=0.0), ARG), (dict(ks=-1.0), ARG), (dict(ks=float("nan")), ARG), (dict(ks=float("inf")), ARG),
     (dict(vs=0.0), ARG), (dict(vs=-0.5), ARG), (dict(vs=float("nan")), ARG), (dict(vs=float("inf")), ARG),
-    (dict(q=None), NULL), (dict(k=None), NULL), (dict(d=96), UNSUP), (dict(Hq=6, Hkv=4), SHAPE),
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(d=48), UNSUP), (dict(Hq=6, Hkv=4), SHAPE),
     (dict(tps=48), ARG), (dict(k=A + 8), ALIGN), (dict(wsb=16), WS),
 ])
 @pytest.mark.parametrize("fn", ["fa_decode_fp8", "fa_decode_int8"])
@@ -122,7 +122,7 @@ def noalloc(q=A, k=A, v=A, bt=None, lens=A, o=A, B=2, Hq=8, Hkv=2, d=128, L=64, 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), NULL), (dict(lens=None), NULL), (dict(B=0), SHAPE), (dict(Hq=6, Hkv=4), SHAPE),
-    (dict(d=96), UNSUP), (dict(bt=A, page=32), UNSUP), (dict(tps=48), ARG), (dict(scale=float("inf")), ARG),
+    (dict(d=48), UNSUP), (dict(bt=A, page=32), UNSUP), (dict(tps=48), ARG), (dict(scale=float("inf")), ARG),
     (dict(k=A + 8), ALIGN),
     # partials beyond the 16 MiB device array
     (dict(B=64, Hq=32, Hkv=8, L=32768, tps=64), WS), (dict(B=2, Hq=64, Hkv=8, d=256, L=65536, tps=256), WS),
@@ -188,7 +188,7 @@ def test_decode_workspace_bytes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(op=None), NULL), (dict(lse=None), NULL), (dict(o=None), NULL),
-    (dict(R=0), SHAPE), (dict(S=0), SHAPE), (dict(d=32), UNSUP), (dict(d=96), UNSUP), (dict(d=512), UNSUP),
+    (dict(R=0), SHAPE), (dict(S=0), SHAPE), (dict(d=16), UNSUP), (dict(d=48), UNSUP), (dict(d=512), UNSUP),
     (dict(op=A + 4), ALIGN), (dict(o=A + 8), ALIGN), (dict(lse=A + 2), ALIGN), (dict(lo=A + 1), ALIGN),
 ])
 def test_merge_rejects(kw, code):

@@ -243,6 +243,14 @@ def decode_paged_d256(poison=False) -> DecodeCase:
                         name="decode_paged_b4h16x8kv1k16kd256", poison=poison)
 
 
+def decode_paged_hd(d: int, poison=False) -> DecodeCase:
+    """Decode at a further head dim d (32 or 96): the shape of the head-dim-256
+    workload, B=4, Hq=16, Hkv=8, mixed lengths U{1024..16384}, page 16,
+    shuffled pool."""
+    return decode_paged(4, 16, 8, d, paged_lengths(1010 + d, 4, 1024, 16384), 16384, seed=1010 + d,
+                        name=f"decode_paged_b4h16x8kv1k16kd{d}", poison=poison)
+
+
 def paged_from_contiguous(case: DecodeCase, seed: int = 99) -> DecodeCase:
     """Scatter a contiguous cache into a shuffled page pool (same values, same
     lengths): the paged view of exactly the same data."""
