@@ -41,6 +41,12 @@ def lib() -> ctypes.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built; run: python -m attention_fa_prefill_amd.build")
+        # libfa.so must run on the HIP runtime that owns the caller's memory and
+        # streams. PyTorch ships its own copy of the runtime; once torch is
+        # loaded, libfa.so's dependency on libamdhip64.so.7 resolves to that
+        # copy. Loaded first, libfa.so would pull in the system runtime and the
+        # process would hold two, whose streams and launches do not mix.
+        _torch()
         L = ctypes.CDLL(LIB_PATH)
         vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.fa_status_string.argtypes = [ci]

@@ -289,11 +289,19 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   int len = p.lens[b];
   len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
   const int tok0 = s * T;
-  if (tok0 >= len) return;  // empty split: the merge never reads it
-  const int tok1 = min(len, tok0 + T);
-  const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
   const int hq0 = g * p.G + hc * 16;
   const int nh = min(16, p.G - hc * 16);
+  if (tok0 >= len) {
+    // empty split: the merge never reads it. (direct: the sequence is empty
+    // and its rows of o are zeros, the value of an empty sum.)
+    if (p.direct) {
+      __bf16* o = (__bf16*)p.o + ((size_t)b * p.Hq + hq0) * D;
+      for (int i = tid; i < nh * D / 8; i += 256) ((uint4*)o)[i] = make_uint4(0, 0, 0, 0);
+    }
+    return;
+  }
+  const int tok1 = min(len, tok0 + T);
+  const int nsteps = (tok1 - tok0 + kStep - 1) / kStep;
   const int Hkv = p.Hkv;
 
   // Pages past the end of the sequence get row 0: their loads have a zero
@@ -521,6 +529,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   if (n < nh) {
     const int hq = hq0 + n;
     float* dst = p.ws_o + (((size_t)b * p.Hq + hq) * p.nsplit + s) * D;
+    __bf16* dst_o = (__bf16*)p.o + ((size_t)b * p.Hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       float acc[4];
@@ -531,9 +540,15 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
         for (int u = 0; u < 4; ++u) x += a[u] * ((const float*)sV0[u])[(db * 4 + r) * 64 + lane];
         acc[r] = x * inv * p.vs;
       }
-      *(float4*)(dst + 16 * db + 4 * cq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      // direct (one split per sequence): this split is the whole sequence and
+      // its normalised output is o, rounded to bf16 as the merge would round
+      // a single split's output (weight exactly 1)
+      if (p.direct)
+        *(uint2*)(dst_o + 16 * db + 4 * cq) = make_uint2(pack2(acc[0], acc[1]), pack2(acc[2], acc[3]));
+      else
+        *(float4*)(dst + 16 * db + 4 * cq) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
-    if (cq == 0) p.ws_lse[((size_t)b * p.Hq + hq) * p.nsplit + s] = (M + log2f(L)) * kLn2;
+    if (cq == 0 && !p.direct) p.ws_lse[((size_t)b * p.Hq + hq) * p.nsplit + s] = (M + log2f(L)) * kLn2;
   }
 }
 
@@ -673,7 +688,7 @@ hipError_t launch_decode(const DecodeParams& p, int d, int fmt, hipStream_t stre
     e = launch_kernel(decode_split_kernel<32, true, true>, grid, block, stream, p);
   else
     return hipErrorInvalidValue;
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || p.direct) return e;  // direct: the split kernel wrote o
   MergeParams m;
   m.o_parts = p.ws_o;
   m.lse = p.ws_lse;

@@ -244,7 +244,11 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   p.nsplit = (max_kv_len + tps - 1) / tps;
   p.G = G;
   p.hchunks = hchunks;
-  p.compact = B <= kCompactMaxB ? 1 : 0;
+  // One split per sequence: the split kernel writes o itself and the merge
+  // launch is skipped (one kernel per call). Every (sequence, head chunk) then
+  // has its work-group, so an empty sequence's rows are written as zeros.
+  p.direct = p.nsplit == 1 ? 1 : 0;
+  p.compact = (B <= kCompactMaxB && !p.direct) ? 1 : 0;
   p.adapt = (tokens_per_split == 0 && p.compact) ? 1 : 0;
   // (d = 256: one split work-group per CU, its registers and LDS allow no second)
   p.cap = d == 256 ? resident_split_groups() / 2 : resident_split_groups();

@@ -72,6 +72,7 @@ struct DecodeParams {
   int adapt;           // compact and default split size: the kernel may enlarge tps
   int cap;             // split work-groups resident at once on this GPU
   int* ws_t;           // the split size the split kernel used (written by work-group 0)
+  int direct;          // one split per sequence (nsplit = 1): the split kernel writes o, no merge
 };
 
 // KV-cache element formats: bf16; one byte per element, OCP FP8 E4M3 codes or

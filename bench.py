@@ -553,13 +553,61 @@ def main():
                     "graph_replay_one_call_isolated_us_p50": round(statistics.median(rep_1), 2),
                     "graph_calls_per_replay": n}
 
+        # a short-context serving batch: one split per sequence, so fa_decode
+        # is one launch (no merge kernel)
+        cb = workloads.decode_batch_short()
+        qb, kb, vb = bf16(cb.q), bf16(cb.kcache), bf16(cb.vcache)
+        lensb, btb = i32(cb.seqlens), i32(cb.block_table)
+        ob = torch.empty_like(qb)
+        needb = fa.decode_workspace_bytes(cb.B, cb.Hq, cb.Hkv, cb.d, cb.max_kv_len, 0)
+        wsb = torch.empty(needb, dtype=torch.uint8, device=dev)
+        assert fa.decode_split_tokens(cb.B, cb.Hq, cb.Hkv, cb.max_kv_len, 0) >= cb.max_kv_len
+
+        def cbcall(st_handle):
+            st = L.fa_decode(ctypes.c_void_p(qb.data_ptr()), ctypes.c_void_p(kb.data_ptr()),
+                             ctypes.c_void_p(vb.data_ptr()), ctypes.c_void_p(btb.data_ptr()),
+                             ctypes.c_void_p(lensb.data_ptr()), ctypes.c_void_p(ob.data_ptr()), cb.B, cb.Hq, cb.Hkv,
+                             cb.d, cb.max_kv_len, 16, 0, cb.scale, ctypes.c_void_p(wsb.data_ptr()), needb, st_handle)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+
         result["launch_modes"] = {
             c1.name: launch_modes(c1call_on),
             c5.name: launch_modes(c5call),
+            cb.name: launch_modes(cbcall),
             "note": "inputs resident, caches warm; back-to-back figures are the mean over 100 calls (median of 5 "
                     "runs); the graph holds 20 calls and is replayed 5 times per run; isolated figures are the "
                     "median of 100 calls, each between its own event pair"}
-        del q5, k5, v5, lens5, bt5, o5, ws5
+        # the same batch through split kernel + merge kernel: a block table
+        # twice as wide (capacity 2048, split size 1024) gives two splits per
+        # sequence, the second always empty, i.e. the same work plus the merge
+        btw = torch.zeros((cb.B, 2 * btb.shape[1]), dtype=torch.int32, device=dev)
+        btw[:, : btb.shape[1]] = btb
+        needw = fa.decode_workspace_bytes(cb.B, cb.Hq, cb.Hkv, cb.d, 2 * cb.max_kv_len, cb.max_kv_len)
+        wsw = torch.empty(needw, dtype=torch.uint8, device=dev)
+
+        def cbcall_two():
+            st = L.fa_decode(ctypes.c_void_p(qb.data_ptr()), ctypes.c_void_p(kb.data_ptr()),
+                             ctypes.c_void_p(vb.data_ptr()), ctypes.c_void_p(btw.data_ptr()),
+                             ctypes.c_void_p(lensb.data_ptr()), ctypes.c_void_p(ob.data_ptr()), cb.B, cb.Hq, cb.Hkv,
+                             cb.d, 2 * cb.max_kv_len, 16, cb.max_kv_len, cb.scale, ctypes.c_void_p(wsw.data_ptr()),
+                             needw, ctypes_stream)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+
+        nb = decode_bytes(cb)
+        one_c = statistics.median(timed_calls(lambda: cbcall(ctypes_stream), args.decode_reps, evict=True))
+        two_c = statistics.median(timed_calls(cbcall_two, args.decode_reps, evict=True))
+        one_w = statistics.median(timed_calls(lambda: cbcall(ctypes_stream), 50, evict=False))
+        two_w = statistics.median(timed_calls(cbcall_two, 50, evict=False))
+        result["decode_one_launch"] = {
+            "workload": cb.name, "algorithmic_bytes": nb,
+            "one_launch_us_p50": round(one_c, 2), "split_plus_merge_us_p50": round(two_c, 2),
+            "one_launch_GB_per_s": round(nb / (one_c * 1e-6) / 1e9, 1),
+            "one_launch_us_p50_warm": round(one_w, 2), "split_plus_merge_us_p50_warm": round(two_w, 2),
+            "note": "one split per sequence: the split kernel writes o (one launch); the comparison runs the same "
+                    "splits through split kernel + merge kernel; caches evicted before each call (warm: not)"}
+        del q5, k5, v5, lens5, bt5, o5, ws5, qb, kb, vb, lensb, btb, ob, wsb, btw, wsw
         torch.cuda.empty_cache()
 
         # ------------------------------------------------------------------ practical ceilings

@@ -206,6 +206,11 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, 
  *
  * Two kernels run in stream order: a split-KV kernel writing per-split
  * (normalised output, log-sum-exp), then the log-sum-exp merge into o.
+ * When every sequence fits one split (max_kv_len <= the split size; the
+ * default gives this for B * Hkv * ceil(G / 16) >= 512 with max_kv_len <=
+ * 1024, or for max_kv_len <= 64), the split kernel writes o itself and the
+ * merge is not launched: one kernel per call, with the bits the merge would
+ * give (a single split has weight exactly 1). The workspace is still required.
  * For the same tokens_per_split and seqlens (the default split size depends on
  * them) the paged and contiguous paths perform the same arithmetic in the same
  * order, so their results are bitwise equal.

@@ -243,11 +243,21 @@ def decode_paged_d256(poison=False) -> DecodeCase:
                         name="decode_paged_b4h16x8kv1k16kd256", poison=poison)
 
 
+def decode_batch_short(poison=False) -> DecodeCase:
+    """A serving batch of short contexts: B=64, Hq=32, Hkv=8, d=128, lengths
+    U{256..1024}, capacity 1024, page 16, shuffled pool. 512 (sequence, kv
+    head) pairs: the default split size gives one split per sequence, so
+    decode runs in one launch."""
+    lens = rng(1011, 21).integers(256, 1025, size=64).astype(np.int32)
+    return decode_paged(64, 32, 8, 128, lens, 1024, seed=1011, name="decode_batch_b64h32x8kv256to1kd128",
+                        poison=poison)
+
+
 def decode_paged_hd(d: int, poison=False) -> DecodeCase:
-    """Decode at a further head dim d (32 or 96): the shape of the head-dim-256
-    workload, B=4, Hq=16, Hkv=8, mixed lengths U{1024..16384}, page 16,
-    shuffled pool."""
-    return decode_paged(4, 16, 8, d, paged_lengths(1010 + d, 4, 1024, 16384), 16384, seed=1010 + d,
+    """Decode at a further head dim d (32 or 96): the head-dim-256 workload's
+    shape and lengths (B=4, Hq=16, Hkv=8, lengths drawn U{1024..16384} with
+    its seed), other values, page 16, shuffled pool."""
+    return decode_paged(4, 16, 8, d, paged_lengths(1009, 4, 1024, 16384), 16384, seed=1010 + d,
                         name=f"decode_paged_b4h16x8kv1k16kd{d}", poison=poison)
 
 
