@@ -14,7 +14,9 @@ namespace {
 constexpr int kMinDefaultTps = 64;
 constexpr int kMaxDefaultTps = 1024;
 constexpr int kTargetSplitGroups = 512;  // two resident split work-groups per CU
+constexpr int kDefaultSplitGroups = 256; // default split size: grid near one work-group per CU
 constexpr int kMaxTps = 2048;
+constexpr int kOneLaunchMaxLen = 512;  // default: one split per sequence up to this capacity
 constexpr int kCompactMaxB = 4096;  // up to 16 sequences scanned per thread of a split work-group
 constexpr int kMaxGridYZ = 65535;
 
@@ -77,14 +79,28 @@ int resident_split_groups() {
 // Work-groups one split of every sequence launches: B * Hkv * ceil(G / 16).
 long split_streams(int B, int Hq, int Hkv) { return (long)B * Hkv * ((Hq / Hkv + 15) / 16); }
 
-// tokens_per_split == 0: the smallest power of two >= 64 that keeps the grid
-// near kTargetSplitGroups work-groups, capped at 1024 (a 256k-token sequence
-// then still has 256 splits). Any other value is taken as given (validated by
-// the caller). Returns 0 for invalid sizes.
+// tokens_per_split == 0: one split per sequence (a single launch: the split
+// kernel writes o and no merge runs) when the capacity is at most
+// kOneLaunchMaxLen tokens, or at most kMaxTps with at least max_kv_len / 8
+// split streams; else the smallest power of two >= 64 that keeps the grid
+// near kDefaultSplitGroups work-groups, capped at 1024 (a 256k-token sequence
+// then still has 256 splits). Measured (caches evicted, d = 128, full
+// lengths): a split work-group reads ~50 GB/s, so one launch wins once the
+// streams together, not one work-group's rate, set the time, or once the
+// merge kernel (several us per call) costs more than a short capacity saves
+// by splitting (max_kv_len 512: one launch at every batch; 1024 from 128
+// streams; 2048 from 256 streams, e.g. 57.6 against 65.7 us at B = 32,
+// Hkv = 8); and fewer, longer splits (about one work-group per CU) beat
+// twice as many half as long (B = 4, max_kv_len 2048: 19.3 against 20.7 us).
+// Any other value is taken as given (validated by the caller). Returns 0
+// for invalid sizes.
 int resolve_tps(int B, int Hq, int Hkv, int max_kv_len, int tps) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_kv_len <= 0 || Hq % Hkv != 0) return 0;
   if (tps != 0) return tps;
-  const long want = ((long)max_kv_len * split_streams(B, Hq, Hkv) + kTargetSplitGroups - 1) / kTargetSplitGroups;
+  const long streams = split_streams(B, Hq, Hkv);
+  if (max_kv_len <= kOneLaunchMaxLen || (max_kv_len <= kMaxTps && 8 * streams >= max_kv_len))
+    return (max_kv_len + 31) / 32 * 32;
+  const long want = ((long)max_kv_len * streams + kDefaultSplitGroups - 1) / kDefaultSplitGroups;
   int t = kMinDefaultTps;
   while (t < kMaxDefaultTps && t < want) t *= 2;
   return t;

@@ -154,10 +154,13 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
  * fa_decode_split_tokens - the KV tokens each split work-group of fa_decode
  * covers (n_split = ceil(max_kv_len / result) splits per sequence; this sizes
  * the workspace).
- * tokens_per_split == 0 asks for the default: the smallest power of two in
- * [64, 1024] for which B * Hkv * ceil((Hq/Hkv)/16) * n_split stays near 512
- * work-groups (two per compute unit), so long sequences are split finely
- * enough to fill the GPU; 1024 keeps a 262144-token sequence at 256 splits.
+ * tokens_per_split == 0 asks for the default. With S = B * Hkv *
+ * ceil((Hq/Hkv)/16) split streams: max_kv_len rounded up to a multiple of 32
+ * (one split per sequence, so fa_decode is one launch) when max_kv_len <= 512,
+ * or when max_kv_len <= 2048 and 8 * S >= max_kv_len; otherwise the smallest
+ * power of two in [64, 1024] for which S * n_split stays near 256 work-groups
+ * (one per compute unit), so long sequences are split finely enough to fill
+ * the GPU; 1024 keeps a 262144-token sequence at 256 splits.
  * With the default and B <= 4096, fa_decode itself may then enlarge the split
  * to 5/4, 3/2 or 2 times this value (a multiple of 32, at most 2048) once it
  * sees seqlens on the device: it takes the size with the fewest tokens per
@@ -207,8 +210,8 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, 
  * Two kernels run in stream order: a split-KV kernel writing per-split
  * (normalised output, log-sum-exp), then the log-sum-exp merge into o.
  * When every sequence fits one split (max_kv_len <= the split size; the
- * default gives this for B * Hkv * ceil(G / 16) >= 512 with max_kv_len <=
- * 1024, or for max_kv_len <= 64), the split kernel writes o itself and the
+ * default gives this for short capacities, see fa_decode_split_tokens), the
+ * split kernel writes o itself and the
  * merge is not launched: one kernel per call, with the bits the merge would
  * give (a single split has weight exactly 1). The workspace is still required.
  * For the same tokens_per_split and seqlens (the default split size depends on

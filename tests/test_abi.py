@@ -158,14 +158,24 @@ def test_decode_split_tokens():
         assert fa.decode_split_tokens(4, 32, 8, 32768, bad) == 0
     assert fa.decode_split_tokens(4, 32, 6, 32768, 0) == 0  # Hq % Hkv != 0
     assert fa.decode_split_tokens(0, 32, 8, 32768, 0) == 0
-    # default: smallest power of two in [64, 1024] with
-    # B * Hkv * ceil(G / 16) * ceil(max_kv_len / tps) <= 512 work-groups
-    for B, Hq, Hkv, L in [(4, 32, 8, 32768), (8, 32, 8, 16384), (1, 16, 2, 262144), (1, 8, 8, 1024),
-                          (1, 1, 1, 1), (2, 64, 2, 4096), (3, 40, 8, 777)]:
+    # default: one split per sequence (max_kv_len rounded up to 32) for
+    # max_kv_len <= 512, or for max_kv_len <= 2048 with 8 * streams >= max_kv_len;
+    # else the smallest power of two in [64, 1024] with
+    # B * Hkv * ceil(G / 16) * ceil(max_kv_len / tps) <= 256 work-groups
+    cases = [(4, 32, 8, 32768), (8, 32, 8, 16384), (1, 16, 2, 262144), (1, 8, 8, 1024), (1, 1, 1, 1),
+             (2, 64, 2, 4096), (3, 40, 8, 777), (1, 1, 1, 512), (1, 1, 1, 513), (64, 32, 8, 1024),
+             (16, 32, 8, 1024), (8, 32, 8, 1024), (32, 32, 8, 2048), (16, 32, 8, 2048), (64, 32, 8, 2049),
+             (4, 64, 2, 100), (128, 8, 8, 4096)]
+    for B, Hq, Hkv, L in cases:
         t = fa.decode_split_tokens(B, Hq, Hkv, L, 0)
         streams = B * Hkv * (-(-(Hq // Hkv) // 16))
-        fits = [x for x in (64, 128, 256, 512, 1024) if streams * L <= 512 * x]
+        if L <= 512 or (L <= 2048 and 8 * streams >= L):
+            assert t == -(-L // 32) * 32 and t >= L, (B, Hq, Hkv, L, t)
+            continue
+        fits = [x for x in (64, 128, 256, 512, 1024) if streams * L <= 256 * x]
         assert t == (fits[0] if fits else 1024), (B, Hq, Hkv, L, t)
+    assert fa.decode_split_tokens(16, 32, 8, 1024, 0) == 1024   # 128 streams: one launch
+    assert fa.decode_split_tokens(8, 32, 8, 1024, 0) == 256     # 64 streams: 4 splits
     # the long-context workload keeps at least 256 splits
     t5 = fa.decode_split_tokens(1, 16, 2, 262144, 0)
     assert -(-262144 // t5) >= 256
