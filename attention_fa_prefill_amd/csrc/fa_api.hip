@@ -238,7 +238,7 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   const int G = Hq / Hkv;
   const int hchunks = (G + 15) / 16;
   const long nsplit_l = ((long)max_kv_len + tps - 1) / tps;
-  if ((long)B * nsplit_l * Hkv * hchunks > (long)INT32_MAX) return FA_ERR_SHAPE;
+  if (((long)B * nsplit_l + 7) / 8 * 8 * Hkv * hchunks > (long)INT32_MAX) return FA_ERR_SHAPE;
   if (!block_table && (size_t)B * (size_t)max_kv_len > (size_t)INT32_MAX) return FA_ERR_SHAPE;
   const size_t need = fa_decode_workspace_bytes(B, Hq, Hkv, d, max_kv_len, tps);
   if (use_scratch) {
@@ -266,6 +266,11 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   p.direct = p.nsplit == 1 ? 1 : 0;
   p.compact = (B <= kCompactMaxB && !p.direct) ? 1 : 0;
   p.adapt = (tokens_per_split == 0 && p.compact) ? 1 : 0;
+  // the work-groups of neighbouring kv heads on one XCD where their row slices
+  // are 32 or 64 bytes (so 4 or 2 of them share every 128-byte line); with
+  // 96-byte slices (d = 96, one-byte cache) the split order measured faster
+  const int slice = d * (bytes ? 1 : 2);
+  p.xcd_group = (slice < 128 && 128 % slice == 0) ? 1 : 0;
   // (d = 256: one split work-group per CU, its registers and LDS allow no second)
   p.cap = d == 256 ? resident_split_groups() / 2 : resident_split_groups();
   // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0;

@@ -73,6 +73,7 @@ struct DecodeParams {
   int cap;             // split work-groups resident at once on this GPU
   int* ws_t;           // the split size the split kernel used (written by work-group 0)
   int direct;          // one split per sequence (nsplit = 1): the split kernel writes o, no merge
+  int xcd_group;       // all (kv head, head chunk) work-groups of a split on one XCD (row slices < 128 B)
 };
 
 // KV-cache element formats: bf16; one byte per element, OCP FP8 E4M3 codes or

@@ -117,7 +117,7 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the decode leg and print its results (not the headline line)")
     ap.add_argument("--decode-reps", type=int, default=50)
-    ap.add_argument("--only", choices=["prefill_cache", "head_dims", "f32_large", "decode_head_dims"],
+    ap.add_argument("--only", choices=["prefill_cache", "head_dims", "f32_large", "decode_head_dims", "decode_d256"],
                     help="run only this leg and print its results (not the headline line); for profiler passes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run 5 plain 256 MiB device-to-device copies (HBM counter calibration)")
@@ -348,15 +348,19 @@ def main():
             "kernel": "prefill_f32_mfma_kernel<128>", "note": "30 back-to-back calls after 30 warm-up calls"}
 
     def leg_decode_head_dims():
-        """decode at head dims 96 and 32 (padded LDS stage rows), the shape of the d = 256 leg"""
+        """decode at head dims 96 and 32 (padded LDS stage rows), the shape and lengths of the d = 256 leg"""
         return decode_leg(makers=(lambda: workloads.decode_paged_hd(96), lambda: workloads.decode_paged_hd(32)))
+
+    def leg_decode_d256():
+        """decode at head dim 256 (one split work-group per CU), bf16 and one-byte caches"""
+        return decode_leg(makers=(workloads.decode_paged_d256,))
 
     if args.decode_only:
         print(json.dumps({"decode": decode_leg()}), flush=True)
         return
     if args.only:
         leg = {"prefill_cache": leg_prefill_cache, "head_dims": leg_head_dims, "f32_large": leg_f32_large,
-               "decode_head_dims": leg_decode_head_dims}[args.only]
+               "decode_head_dims": leg_decode_head_dims, "decode_d256": leg_decode_d256}[args.only]
         print(json.dumps({args.only: leg()}), flush=True)
         return
 
@@ -446,9 +450,9 @@ def main():
         result["prefill_head_dims"] = leg_head_dims()
         result["prefill_f32_large"] = leg_f32_large()
 
-        # decode at head dim 256 (one split work-group per CU), bf16 and FP8
-        # caches, timed like the decode legs above
-        result["decode_head_dim_256"] = decode_leg(makers=(workloads.decode_paged_d256,))
+        # decode at head dim 256 (one split work-group per CU), bf16 and
+        # one-byte caches, timed like the decode legs above
+        result["decode_head_dim_256"] = leg_decode_d256()
         # decode at head dims 96 and 32 (padded LDS stage rows), the same shape
         result["decode_head_dims_96_32"] = leg_decode_head_dims()
 

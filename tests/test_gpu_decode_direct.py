@@ -62,7 +62,7 @@ def test_one_launch_equals_two_kernel_path(fmt):
     assert_bf16_close(got, ref(case), case.name)
 
 
-@pytest.mark.parametrize("d", [64, 96, 256])
+@pytest.mark.parametrize("d", [32, 64, 96, 256])
 def test_one_launch_head_dims(d):
     B, Hq, Hkv, cap = 24, 16, 4, 512
     case = workloads.decode_paged(B, Hq, Hkv, d, short_lengths(71 + d, B, cap), cap, seed=71 + d)
@@ -79,6 +79,18 @@ def test_one_launch_head_groups(G, Hkv):
     o1 = run(case, cap)
     assert np.array_equal(host_bits(o1), host_bits(run(widened(case, 2 * cap), cap)))
     assert_bf16_close(host_f64(o1), oracle_out(case), case.name)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_one_launch_byte_cache_d64(fmt):
+    """d = 64 over a one-byte cache: 64-byte row slices, the work-groups of
+    neighbouring kv heads grouped on one XCD."""
+    make, runner, ref = FORMATS[fmt]
+    B, cap = 24, 512
+    case = make(workloads.decode_paged(B, 16, 4, 64, short_lengths(85, B, cap), cap, seed=85))
+    o1 = runner(case, cap)
+    assert np.array_equal(host_bits(o1), host_bits(runner(widened(case, 2 * cap), cap)))
+    assert_bf16_close(host_f64(o1), ref(case), case.name)
 
 
 def test_one_launch_contiguous_equals_paged():
