@@ -104,6 +104,45 @@ def traffic_for(kernel_key, src_path):
     return ent.get("bytes_per_launch")
 
 
+def smi_clocks_under_load(step, torch, max_s=20.0):
+    """Run `amd-smi metric -c --json` in a child process while `step` is
+    issued back to back; return the graphics clocks (per XCD) and memory clock
+    it reports, or the error."""
+    import subprocess
+    import threading
+
+    res = {}
+
+    def query():
+        try:
+            out = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                                 timeout=max_s).stdout
+            res["data"] = json.loads(out)
+        except Exception as e:  # noqa: BLE001 - reported, never fatal
+            res["error"] = repr(e)[:200]
+
+    th = threading.Thread(target=query)
+    t0 = time.perf_counter()
+    th.start()
+    while th.is_alive() and time.perf_counter() - t0 < max_s:
+        for _ in range(50):
+            step()
+        torch.cuda.synchronize()
+    th.join()
+    if "data" not in res:
+        return {"source": "amd-smi metric -c --json", "error": res.get("error", "no output")}
+    try:
+        clk = res["data"]["gpu_data"][0]["clock"]
+        gfx = [v["clk"]["value"] for k, v in sorted(clk.items()) if k.startswith("gfx") and isinstance(v, dict)]
+        mx = [v["max_clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v, dict)]
+        mem = [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem") and isinstance(v, dict)
+               and isinstance(v.get("clk"), dict)]
+        return {"source": "amd-smi metric -c --json, sampled during back-to-back headline calls",
+                "gfx_mhz_per_xcd": gfx, "gfx_max_mhz": max(mx) if mx else None, "mem_mhz": mem[0] if mem else None}
+    except (KeyError, IndexError, TypeError, ValueError) as e:
+        return {"source": "amd-smi metric -c --json", "error": "unexpected format: " + repr(e)[:100]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -384,6 +423,9 @@ def main():
             step()
         torch.cuda.synchronize()
         n_settle += 50
+    # GPU clocks as the driver reports them, sampled (amd-smi, a child
+    # process) while the headline call runs back to back
+    clocks = smi_clocks_under_load(step, torch)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -426,7 +468,8 @@ def main():
               "config": {"workload": case.name, "B": B, "Hq": Hq, "Hkv": Hkv, "Sq": Sq, "Skv": Skv, "d": d,
                          "causal": True, "scale": case.scale, "seed": 1002},
               "roofline": roofline,
-              "prefill_us_per_call_p50": round(statistics.median(launch_ms) * 1e3, 2)}
+              "prefill_us_per_call_p50": round(statistics.median(launch_ms) * 1e3, 2),
+              "gpu_clocks_under_load": clocks}
 
     # ------------------------------------------------------------------ decode and latency legs
     if not args.prefill_only:
