@@ -96,3 +96,23 @@ def test_merge_lse(d):
     ref_o, ref_l = oracle.merge(op.astype(np.float64), ls.astype(np.float64))
     assert np.max(np.abs(host_f64(o) - ref_o)) <= F32_MAX_ABS
     assert np.max(np.abs(host_f64(lse_out) - ref_l)) <= F32_MAX_ABS
+
+
+@pytest.mark.parametrize("B", [300, 4100])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+def test_d32_many_sequences_and_head_chunks(B, fmt):
+    """d = 32 (row slices of 64 or 32 bytes: the work-groups of all kv heads
+    and head chunks of a split on one XCD) with G = 32 (two head chunks per kv
+    head), B above and below the batch that is scanned per work-group, short
+    mixed lengths with zeros, poisoned slots."""
+    lens = np.random.default_rng(B + 7).integers(0, 97, size=B).astype(np.int32)
+    case = workloads.decode_contiguous(B, 64, 2, 32, 96, seqlens=lens, seed=37, poison=True)
+    if fmt == "fp8":
+        case = workloads.as_fp8(case)
+        o, ref = run_fp8(case, 32), oracle_out_fp8(case)
+    else:
+        o, ref = run(case, 32), oracle_out(case)
+    got = host_f64(o)
+    assert np.all(got[lens == 0] == 0.0)
+    assert np.all(np.isfinite(got))
+    assert_bf16_close(got, ref, f"d=32 B={B} {fmt}")
