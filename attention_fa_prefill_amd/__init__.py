@@ -46,7 +46,11 @@ def lib() -> ctypes.CDLL:
         # loaded, libfa.so's dependency on libamdhip64.so.7 resolves to that
         # copy. Loaded first, libfa.so would pull in the system runtime and the
         # process would hold two, whose streams and launches do not mix.
-        _torch()
+        # (Without torch there is only the system runtime.)
+        try:
+            _torch()
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         L.fa_status_string.argtypes = [ci]
