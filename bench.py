@@ -104,41 +104,49 @@ def traffic_for(kernel_key, src_path):
     return ent.get("bytes_per_launch")
 
 
-def smi_clocks_under_load(step, torch, max_s=20.0):
-    """Run `amd-smi metric -c --json` in a child process while `step` is
-    issued back to back; return the graphics clocks (per XCD) and memory clock
-    it reports, or the error."""
+def smi_clocks_under_load(step, torch, samples=3, max_s=20.0):
+    """Run `amd-smi metric -c --json` in a child process `samples` times while
+    `step` is issued back to back; return the graphics clocks (per XCD, per
+    sample, and their median over samples) and the memory clock it reports,
+    or the error. The tool reads the clocks at one instant, so one sample can
+    land in a short idle gap; the median over samples is the figure to use."""
     import subprocess
     import threading
 
-    res = {}
+    res = {"data": []}
 
     def query():
         try:
-            out = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
-                                 timeout=max_s).stdout
-            res["data"] = json.loads(out)
+            for _ in range(samples):
+                out = subprocess.run(["amd-smi", "metric", "-c", "--json"], capture_output=True, text=True,
+                                     timeout=max_s).stdout
+                res["data"].append(json.loads(out))
         except Exception as e:  # noqa: BLE001 - reported, never fatal
             res["error"] = repr(e)[:200]
 
     th = threading.Thread(target=query)
     t0 = time.perf_counter()
     th.start()
-    while th.is_alive() and time.perf_counter() - t0 < max_s:
-        for _ in range(50):
+    while th.is_alive() and time.perf_counter() - t0 < samples * max_s:
+        for _ in range(200):
             step()
         torch.cuda.synchronize()
     th.join()
-    if "data" not in res:
+    if not res["data"]:
         return {"source": "amd-smi metric -c --json", "error": res.get("error", "no output")}
     try:
-        clk = res["data"]["gpu_data"][0]["clock"]
-        gfx = [v["clk"]["value"] for k, v in sorted(clk.items()) if k.startswith("gfx") and isinstance(v, dict)]
-        mx = [v["max_clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v, dict)]
-        mem = [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem") and isinstance(v, dict)
-               and isinstance(v.get("clk"), dict)]
+        per_sample, mx, mem = [], [], []
+        for d in res["data"]:
+            clk = d["gpu_data"][0]["clock"]
+            per_sample.append([v["clk"]["value"] for k, v in sorted(clk.items())
+                               if k.startswith("gfx") and isinstance(v, dict)])
+            mx += [v["max_clk"]["value"] for k, v in clk.items() if k.startswith("gfx") and isinstance(v, dict)]
+            mem += [v["clk"]["value"] for k, v in clk.items() if k.startswith("mem") and isinstance(v, dict)
+                    and isinstance(v.get("clk"), dict)]
+        med = [statistics.median(x) for x in zip(*per_sample)]
         return {"source": "amd-smi metric -c --json, sampled during back-to-back headline calls",
-                "gfx_mhz_per_xcd": gfx, "gfx_max_mhz": max(mx) if mx else None, "mem_mhz": mem[0] if mem else None}
+                "gfx_mhz_per_xcd_median": med, "gfx_mhz_per_xcd_samples": per_sample,
+                "gfx_max_mhz": max(mx) if mx else None, "mem_mhz": mem[0] if mem else None}
     except (KeyError, IndexError, TypeError, ValueError) as e:
         return {"source": "amd-smi metric -c --json", "error": "unexpected format: " + repr(e)[:100]}
 
