@@ -53,10 +53,10 @@ constexpr float kTau = 8.0f;   // lazy rescale threshold (log2 units)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// V staging swizzle: 16-byte chunk XOR 2*(row % 8) (D=128, 256) / 2*(row % 4) (D=64),
-// so the 4-row x 32-byte footprint of each transpose read hits distinct banks.
-// (CP: 16-byte chunks per LDS row of the stage, a power of two; rows of
-// d = 96 are padded to it)
+// V staging swizzle: 16-byte chunk XOR 2*(row % 8) with 16 or more chunks per
+// LDS row, 2*(row % (CP/2)) with fewer, so the 4-row x 32-byte footprint of
+// each transpose read hits distinct banks. (CP: 16-byte chunks per LDS row of
+// the stage, a power of two; rows of d = 96 are padded to it.)
 template <int CP>
 __device__ __forceinline__ int swz_v(int row) { return 2 * (row & (CP >= 16 ? 7 : CP / 2 - 1)); }
 // FP8 V staging swizzle. A transpose read of 8-bit elements (ds_read_b64_tr_b8)
