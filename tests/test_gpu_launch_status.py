@@ -57,6 +57,7 @@ def test_prefill_and_decode_ignore_a_pending_error():
     left = hip.hipGetLastError()  # collect (and clear) whatever is pending before torch runs again
     print(f"planted {planted}; fa_prefill -> {st}; pending afterwards {left}", flush=True)
     assert st == fa.FA_OK
+    assert left == planted  # neither reported nor cleared by the call
 
     planted = plant_error(hip)
     st = L.fa_decode(P(dq), P(dk), P(dv), P(bt), P(lens), P(od), dc.B, dc.Hq, dc.Hkv, dc.d, dc.max_kv_len, 16, 0,
@@ -64,6 +65,7 @@ def test_prefill_and_decode_ignore_a_pending_error():
     left = hip.hipGetLastError()
     print(f"planted {planted}; fa_decode -> {st}; pending afterwards {left}", flush=True)
     assert st == fa.FA_OK
+    assert left == planted  # neither reported nor cleared by the call
     torch.cuda.synchronize()
 
     ref, _ = oracle.attention(*pc.as_f64(), pc.scale, True)
