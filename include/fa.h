@@ -47,8 +47,9 @@
  *   - A launch error returns FA_ERR_HIP. Only the status of this call's own
  *     launches is reported: an error left pending by earlier runtime calls is
  *     neither reported nor cleared (the library never calls hipGetLastError).
- *     fa_decode and fa_decode_fp8 launch two kernels; if the second launch
- *     fails, the first has been enqueued. Faults inside a kernel surface, as
+ *     The decode entry points launch two kernels (one when every sequence
+ *     fits one split); if the second launch fails, the first has been
+ *     enqueued. Faults inside a kernel surface, as
  *     with any HIP work, at the caller's next synchronisation.
  *   - The library keeps no mutable global state and is re-entrant; calls on
  *     different streams that share a workspace race.
