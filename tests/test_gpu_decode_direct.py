@@ -179,3 +179,15 @@ def test_short_context_batch_workload():
     o = run(case)
     assert_bf16_close(host_f64(o), oracle_out(case), case.name)
     assert np.array_equal(host_bits(o), host_bits(run(workloads.decode_batch_short(poison=True))))
+
+
+def test_one_launch_at_the_largest_split():
+    """max_kv_len 2048 with 256 split streams: the default is one split of
+    2048 tokens (the largest) per sequence, 128 pages per work-group."""
+    B, Hq, Hkv, d, cap = 32, 32, 8, 64, 2048
+    assert fa.decode_split_tokens(B, Hq, Hkv, cap, 0) == cap
+    lens = short_lengths(95, B, cap)
+    case = workloads.decode_paged(B, Hq, Hkv, d, lens, cap, seed=95)
+    o1 = run(case)
+    assert np.array_equal(host_bits(o1), host_bits(run(widened(case, 2 * cap), cap)))
+    assert_bf16_close(host_f64(o1), oracle_out(case), case.name)
