@@ -142,8 +142,16 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 // p.vs is applied to each split's output; K and V are widened to bf16
 // exactly, so the arithmetic is that of the bf16 cache on the dequantised
 // values.
+// Waves per SIMD the split kernel is compiled for: one-byte caches at d <= 128
+// keep their registers and LDS within three work-groups per CU (a step there
+// moves half the bytes for the same per-token work, so more waves keep more
+// bytes in flight); bf16 two; d = 256 one.
+template <int D, bool F8>
+constexpr int split_waves_per_simd() { return D > 128 ? 1 : (F8 ? 3 : 2); }
+
 template <int D, bool F8, bool I8>
-__global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(split_waves_per_simd<D, F8>())))
+decode_split_kernel(DecodeParams p) {
   static_assert(F8 || !I8, "the int8 cache is a one-byte cache");
   auto byte8_to_bf16 = [](u32x2 x) __attribute__((always_inline)) {
     if constexpr (I8)
@@ -164,11 +172,13 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
   constexpr int RI = 64 / CP;        // V rows per direct-to-LDS load (bf16 D=128: 4; fp8: 8)
   constexpr int VDMA = kStep / RI;   // direct-to-LDS loads per step
   constexpr int NLD = 2 * KS + VDMA; // vector-memory instructions issued per step
-  // Two V stages per wave (the step being used and the one in flight); an
-  // FP8 step uses the first half of a stage. sV0 doubles as the exchange of
-  // the 4 waves' states at the end.
-  // (sized for bf16 rows: the exchange at the end needs 64 D bytes per wave)
-  constexpr int STG = kStep * pow2_at_least(D / 8, 4) * 8;
+  // Two V stages per wave (the step being used and the one in flight), kStep
+  // rows of RB bytes each (sized in bf16 units). Together they also hold the
+  // exchange of the 4 waves' states at the end: 32-dim-block halves of O^T,
+  // blocks [0, HD) in the first stage and [HD, DB) in the second.
+  constexpr int STG = kStep * RB / 2;
+  constexpr int HD = (DB + 1) / 2;
+  static_assert(HD * 4 * 64 * 4 <= STG * 2, "a stage holds half of a wave's O^T");
   __shared__ __attribute__((aligned(1024))) __bf16 sV0[4][STG];
   __shared__ __attribute__((aligned(1024))) __bf16 sV1[4][STG];
   __shared__ float sM[4][64], sL[4][64];
@@ -521,11 +531,14 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
 
   // ---- merge the 4 waves: O^T lane (n, cq) reg r is dim 16 db + 4 cq + r of head n.
   __syncthreads();
-  float* xo = (float*)sV0[w];
+  // exchange slot of 16-dim block db, register r, of wave u's O^T
+  auto xslot = [&](int u, int db, int r) __attribute__((always_inline)) {
+    return (db < HD ? (float*)sV0[u] : (float*)sV1[u]) + ((db % HD) * 4 + r) * 64 + lane;
+  };
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) xo[(db * 4 + r) * 64 + lane] = O[db][r];
+    for (int r = 0; r < 4; ++r) *xslot(w, db, r) = O[db][r];
   sM[w][lane] = m_run;
   sL[w][lane] = l_run;
   __syncthreads();
@@ -556,7 +569,7 @@ __global__ void __launch_bounds__(256) decode_split_kernel(DecodeParams p) {
       for (int r = 0; r < 4; ++r) {
         float x = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) x += a[u] * ((const float*)sV0[u])[(db * 4 + r) * 64 + lane];
+        for (int u = 0; u < 4; ++u) x += a[u] * *xslot(u, db, r);
         acc[r] = x * inv * p.vs;
       }
       // direct (one split per sequence): this split is the whole sequence and
