@@ -22,8 +22,8 @@
 //     padding chunks are filled with zeros by out-of-range buffer loads;
 //   - d = 256 needs O^T (128 registers) and Q^T (64) per wave, so it runs one
 //     wave per SIMD with up to 512 registers and 128 KB of LDS per work-group;
-//     d = 32 runs two or more work-groups per CU, whose waves overlap each
-//     other's MFMA and softmax phases;
+//     d = 32 runs four work-groups per CU, whose waves overlap each other's
+//     MFMA and softmax phases;
 //   - d = 256 grids of fewer than two rounds of 128-row tiles (one work-group
 //     per CU) run prefill_hd_ks_kernel instead: 64-row tiles whose keys are
 //     split between two wave pairs (below).
@@ -50,7 +50,10 @@ struct HdCfg {
   static constexpr int DB = D / 32;                        // 32-dim blocks of O^T
   static constexpr int NI = kKN * RP / 64 / 4;             // direct-to-LDS loads per wave per block
   static constexpr int STAGE = kKN * RP * 8;               // bf16 elements per LDS stage of K or V
-  static constexpr int OCC = D > 128 ? 1 : 2;              // waves per SIMD the registers allow
+  // waves per SIMD the kernel is compiled for: d = 256 needs all registers;
+  // d = 32 fits in 97 registers at four (four work-groups per CU, whose
+  // softmax and MFMA phases overlap: 13 % faster at B = 4 than at two)
+  static constexpr int OCC = D > 128 ? 1 : (D <= 32 ? 4 : 2);
 };
 
 // K rows are read 16 bytes per lane for 32 consecutive rows at one chunk:
