@@ -525,12 +525,37 @@ def main():
         # empty-work floor: the same stream, a 1-element fill (one trivial kernel)
         tiny = torch.empty(1, device=dev)
         tf = timed_calls(lambda: tiny.fill_(0.0), 200, evict=False)
+        # decode of one chat-length sequence (B = 1, 4096 tokens), warm and cold
+        cc = workloads.decode_b1_chat()
+        qc, kcc, vcc = bf16(cc.q), bf16(cc.kcache), bf16(cc.vcache)
+        lc, btc = i32(cc.seqlens), i32(cc.block_table)
+        oc = torch.empty_like(qc)
+        needc = fa.decode_workspace_bytes(cc.B, cc.Hq, cc.Hkv, cc.d, cc.max_kv_len, 0)
+        wsc = torch.empty(needc, dtype=torch.uint8, device=dev)
+
+        def cccall():
+            st = L.fa_decode(ctypes.c_void_p(qc.data_ptr()), ctypes.c_void_p(kcc.data_ptr()),
+                             ctypes.c_void_p(vcc.data_ptr()), ctypes.c_void_p(btc.data_ptr()),
+                             ctypes.c_void_p(lc.data_ptr()), ctypes.c_void_p(oc.data_ptr()), cc.B, cc.Hq, cc.Hkv,
+                             cc.d, cc.max_kv_len, 16, 0, cc.scale, ctypes.c_void_p(wsc.data_ptr()), needc,
+                             ctypes_stream)
+            if st != 0:
+                raise RuntimeError(fa.status_string(st))
+
+        tcw = timed_calls(cccall, 200, evict=False)
+        tcc = timed_calls(cccall, args.decode_reps, evict=True)
+        del qc, kcc, vcc, lc, btc, oc, wsc
+
         result["latency_b1"] = {
             c1.name: {"us_per_call_p50": round(statistics.median(t1), 2),
                       "us_p10": round(float(np.percentile(t1, 10)), 2)},
             "single_trivial_kernel_floor_us_p50": round(statistics.median(tf), 2),
             case.name: {"us_per_call_p50": result["prefill_us_per_call_p50"]},
             "decode_long_b1h16x2kv256kd128": {"us_per_call_p50": long["us_per_call_p50"]},
+            cc.name: {"us_per_call_p50_warm": round(statistics.median(tcw), 2),
+                      "us_per_call_p50_cold": round(statistics.median(tcc), 2),
+                      "tokens_per_split": fa.decode_split_tokens(cc.B, cc.Hq, cc.Hkv, cc.max_kv_len, 0),
+                      "algorithmic_bytes": decode_bytes(cc)},
         }
 
         # ------------------------------------------------------------------ launch modes (C1 and C5)

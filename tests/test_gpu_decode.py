@@ -146,6 +146,13 @@ def test_many_short_sequences(B):
     assert_bf16_close(got, oracle_out(case), f"B={B}")
 
 
+def test_b1_chat_length_workload():
+    """The bench's latency case: one sequence of 4096 cached tokens (B = 1,
+    Hq = 32, Hkv = 8, paged), every element against the oracle."""
+    case = workloads.decode_b1_chat()
+    assert_bf16_close(host_f64(run(case)), oracle_out(case), case.name)
+
+
 def test_seqlens_clamped_to_capacity():
     lens = np.array([5000, -3], np.int32)  # above capacity and negative
     case = workloads.decode_contiguous(2, 4, 2, 128, 96, seqlens=lens, seed=23)

@@ -253,6 +253,13 @@ def decode_batch_short(poison=False) -> DecodeCase:
                         poison=poison)
 
 
+def decode_b1_chat(poison=False) -> DecodeCase:
+    """One sequence of a chat-length context: B=1, Hq=32, Hkv=8, d=128, 4096
+    cached tokens, page 16, shuffled pool (the latency case of decode)."""
+    return decode_paged(1, 32, 8, 128, np.array([4096], np.int32), 4096, seed=1012,
+                        name="decode_b1h32x8kv4kd128", poison=poison)
+
+
 def decode_paged_hd(d: int, poison=False) -> DecodeCase:
     """Decode at a further head dim d (32 or 96): the head-dim-256 workload's
     shape and lengths (B=4, Hq=16, Hkv=8, lengths drawn U{1024..16384} with
