@@ -315,9 +315,18 @@ decode_split_kernel(DecodeParams p) {
     b = item / p.nsplit;
   }
   const int g = gh / p.hchunks, hc = gh % p.hchunks;
+  const int tok0 = s * T;
+  // This split's pages of the block table are read before the length, as
+  // their addresses do not depend on it (the two reads overlap instead of
+  // following each other): thread i reads the page tok0 / 16 + i of the
+  // split's at most T / 16, within the row; entries past the sequence's last
+  // page are read but not used.
+  static_assert(kPageSlots <= 256, "one page slot per thread");
+  const int my_pg = tok0 / 16 + tid;
+  int my_page = 0;
+  if (p.bt && tid * 16 < T && my_pg < p.pages_per_seq) my_page = p.bt[(size_t)b * p.pages_per_seq + my_pg];
   int len = p.lens[b];
   len = len < 0 ? 0 : (len > p.max_len ? p.max_len : len);
-  const int tok0 = s * T;
   const int hq0 = g * p.G + hc * 16;
   const int nh = min(16, p.G - hc * 16);
   if (tok0 >= len) {
@@ -336,12 +345,7 @@ decode_split_kernel(DecodeParams p) {
   // Pages past the end of the sequence get row 0: their loads have a zero
   // record count and never touch memory.
   const int npg = (tok1 - tok0 + 15) / 16;
-  for (int i = tid; i < kPageSlots; i += 256) {
-    const int pg = tok0 / 16 + i;
-    int row0 = 0;
-    if (i < npg) row0 = p.bt ? p.bt[(size_t)b * p.pages_per_seq + pg] * 16 : b * p.max_len + pg * 16;
-    sRow0[i] = row0;
-  }
+  if (tid < kPageSlots) sRow0[tid] = tid < npg ? (p.bt ? my_page * 16 : b * p.max_len + my_pg * 16) : 0;
   __syncthreads();
 
   const int n = lane & 15, cq = lane >> 4;  // MFMA column (head / token) and k-group

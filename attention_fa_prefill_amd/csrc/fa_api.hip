@@ -264,15 +264,21 @@ fa_status decode_common(const void* q, const void* kcache, const void* vcache, c
   // launch is skipped (one kernel per call). Every (sequence, head chunk) then
   // has its work-group, so an empty sequence's rows are written as zeros.
   p.direct = p.nsplit == 1 ? 1 : 0;
-  p.compact = (B <= kCompactMaxB && !p.direct) ? 1 : 0;
+  // (d = 256: one split work-group per CU, its registers and LDS allow no second)
+  p.cap = d == 256 ? resident_split_groups() / 2 : resident_split_groups();
+  // One sequence whose splits all fit one round of resident work-groups, or
+  // whose split size is given: the device-side choice of the split size would
+  // keep tps (one round at tps is the least), so the scan over seqlens has
+  // nothing to do. Its splits are numbered in order instead, and a work-group
+  // knows its split (and its block-table entries) before it reads the length.
+  const bool one_plain = B == 1 && (tokens_per_split != 0 || (long)Hkv * hchunks * p.nsplit <= p.cap);
+  p.compact = (B <= kCompactMaxB && !p.direct && !one_plain) ? 1 : 0;
   p.adapt = (tokens_per_split == 0 && p.compact) ? 1 : 0;
   // the work-groups of neighbouring kv heads on one XCD where their row slices
   // are 32 or 64 bytes (so 4 or 2 of them share every 128-byte line); with
   // 96-byte slices (d = 96, one-byte cache) the split order measured faster
   const int slice = d * (bytes ? 1 : 2);
   p.xcd_group = (slice < 128 && 128 % slice == 0) ? 1 : 0;
-  // (d = 256: one split work-group per CU, its registers and LDS allow no second)
-  p.cap = d == 256 ? resident_split_groups() / 2 : resident_split_groups();
   // as in prefill: c > 0 even for scale = 0, so a masked score's exp2 is 0;
   // a one-byte cache's K scale multiplies every score, so it joins c
   p.c = fmaxf(fabsf(scale) * (bytes ? k_scale : 1.0f) * fa::kLog2e, 1e-30f);

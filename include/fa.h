@@ -166,7 +166,8 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
  * to 5/4, 3/2 or 2 times this value (a multiple of 32, at most 2048) once it
  * sees seqlens on the device: it takes the size with the fewest tokens per
  * work-group slot over the rounds of resident split work-groups (two per
- * compute unit) that the live splits need, the smallest on a tie. Splits only
+ * compute unit, one at d = 256) that the live splits need, the smallest on a
+ * tie. Splits only
  * get larger, so the workspace always suffices.
  * Any other value must be a positive multiple of 32, at most 2048, and is
  * returned unchanged and used as given. Returns 0 for invalid arguments.
@@ -194,7 +195,10 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int d, int max_kv_len, 
  *                          block_table int32 [B, ceil(max_kv_len/16)], entry
  *                          [b][p] is the physical page of tokens 16p..16p+15 of
  *                          sequence b; entries p >= ceil(seqlens[b]/16) are never
- *                          read; page indices must be in range (not checked).
+ *                          used and may hold anything (they may be read, within
+ *                          the row, before seqlens is known, so the whole table
+ *                          must be allocated); the pages used must be in range
+ *                          (not checked).
  *   seqlens     : int32 [B] device array, tokens cached for each sequence,
  *                 clamped to [0, max_kv_len]; length 0 gives o = 0.
  *   page_size   : must be 16 when block_table != NULL (ignored otherwise).

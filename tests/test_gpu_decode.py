@@ -5,6 +5,7 @@ element with the fp64 oracle; the paged path is checked to reproduce the
 contiguous path bit for bit on the same data; poisoned cache slots (NaN past
 each sequence's length and in unused pages) must not reach the output.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -153,6 +154,25 @@ def test_b1_chat_length_workload():
     assert_bf16_close(host_f64(run(case)), oracle_out(case), case.name)
 
 
+@pytest.mark.parametrize("lens,cap", [([1000], 8192), ([4000], 4096), ([1000, 1, 0, 3000], 4096), ([200, 17], 512)],
+                         ids=["one_sequence_short", "one_sequence_full", "batch", "one_launch"])
+def test_table_entries_past_the_last_page_are_not_used(lens, cap):
+    """Block-table entries at or past ceil(len / 16) may hold anything (one
+    sequence: they are read, within the row, before the length): with page
+    numbers far out of range there, the output is bit for bit the output with
+    the generator's entries, and matches the oracle."""
+    case = workloads.decode_paged(len(lens), 16, 4, 128, np.array(lens, np.int32), cap, seed=53)
+    ref = host_bits(run(case))
+    bt = case.block_table.copy()
+    for b, L in enumerate(lens):
+        n = -(-L // 16)
+        bt[b, n:] = np.where(np.arange(bt.shape[1] - n) % 2 == 0, np.int32(2**31 - 1), np.int32(-(2**31)))
+    junk = dataclasses.replace(case, block_table=bt)
+    got = run(junk)
+    assert np.array_equal(host_bits(got), ref)
+    assert_bf16_close(host_f64(got), oracle_out(case), case.name)
+
+
 def test_seqlens_clamped_to_capacity():
     lens = np.array([5000, -3], np.int32)  # above capacity and negative
     case = workloads.decode_contiguous(2, 4, 2, 128, 96, seqlens=lens, seed=23)
@@ -258,8 +278,15 @@ def _default_split_size(case, t0, cap):
     return best[1]
 
 
+def _one_sequence_72k():
+    """B = 1 with 8 kv heads and 72k tokens: 576 splits of the default 1024
+    tokens overrun one round of resident work-groups; 1280 fit one."""
+    return workloads.decode_paged(1, 32, 8, 128, np.array([73728], np.int32), 73728, seed=47,
+                                  name="decode_b1h32x8kv72kd128")
+
+
 @pytest.mark.parametrize("make", [workloads.decode_contig_32k, workloads.decode_paged_mixed,
-                                  workloads.decode_long_256k])
+                                  workloads.decode_long_256k, _one_sequence_72k])
 def test_default_split_size_chosen_on_device(make):
     """With the default split size the kernel picks its split size from seqlens;
     the size it reports in the workspace follows the documented rule, and the
