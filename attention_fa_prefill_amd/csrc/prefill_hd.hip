@@ -24,9 +24,10 @@
 //     wave per SIMD with up to 512 registers and 128 KB of LDS per work-group;
 //     d = 32 runs four work-groups per CU, whose waves overlap each other's
 //     MFMA and softmax phases;
-//   - d = 256 grids of fewer than two rounds of 128-row tiles (one work-group
-//     per CU) run prefill_hd_ks_kernel instead: 64-row tiles whose keys are
-//     split between two wave pairs (below).
+//   - prefill without a cache runs prefill_hd_ks_kernel instead at d = 32,
+//     and at d = 256 on grids of fewer than two rounds of 128-row tiles (one
+//     work-group per CU): 64-row tiles whose keys are split between two wave
+//     pairs (below).
 #include "fa_internal.h"
 
 namespace fa {
@@ -50,9 +51,10 @@ struct HdCfg {
   static constexpr int DB = D / 32;                        // 32-dim blocks of O^T
   static constexpr int NI = kKN * RP / 64 / 4;             // direct-to-LDS loads per wave per block
   static constexpr int STAGE = kKN * RP * 8;               // bf16 elements per LDS stage of K or V
-  // waves per SIMD the kernel is compiled for: d = 256 needs all registers;
-  // d = 32 fits in 97 registers at four (four work-groups per CU, whose
-  // softmax and MFMA phases overlap: 13 % faster at B = 4 than at two)
+  // waves per SIMD the kernels are compiled for: d = 256 needs all registers;
+  // d = 32 fits at four (97 registers in the one-group kernel, 73 in the
+  // key-split one; four work-groups per CU, whose softmax and MFMA phases
+  // overlap: the one-group kernel ran 13 % faster at B = 4 than at two)
   static constexpr int OCC = D > 128 ? 1 : (D <= 32 ? 4 : 2);
 };
 
@@ -349,19 +351,21 @@ prefill_hd_kernel(PrefillParams p) {
   }
 }
 
-// d = 256 with the keys of each tile split between two wave pairs: a
-// work-group owns a 64-row query tile; waves 2kh and 2kh+1 own its two 32-row
-// halves over the 32-key blocks kh, kh+2, kh+4, ... (kh = 0, 1), and the two
-// partial states of each row are merged through LDS at the end. Against one
-// wave per 32 rows over all keys this halves the longest chain of blocks in a
-// causal grid, and the 64-row tiles (twice as many work-groups, most keys
-// first) fill the CUs in two balanced rounds where 128-row tiles made one
-// unbalanced round.
+// The keys of each tile split between two wave pairs: a work-group owns a
+// 64-row query tile; waves 2kh and 2kh+1 own its two 32-row halves over the
+// 32-key blocks kh, kh+2, kh+4, ... (kh = 0, 1), and the two partial states of
+// each row are merged through LDS at the end. Against one wave per 32 rows
+// over all keys this halves the longest chain of blocks in a causal grid, and
+// the 64-row tiles (twice as many work-groups, most keys first) balance the
+// CUs: at d = 256 they fill two rounds where 128-row tiles made one
+// unbalanced round. At d = 32 (73 registers, 32 KB, four work-groups per CU)
+// a block's work is short against the latency of its loads, and twice as
+// many independent chains of half the length keep more of them in flight.
 constexpr int kTileKs = 64;  // query rows per work-group
 constexpr int kKBKs = 32;    // keys per block
 
 template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HdCfg<D>::OCC, HdCfg<D>::OCC)))
 prefill_hd_ks_kernel(PrefillParams p) {
   using C = HdCfg<D>;
   constexpr int STG = kKBKs * C::RP * 8;      // bf16 elements of one 32-key block
@@ -593,12 +597,14 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
     else
       return hipErrorInvalidValue;
   }
-  // d = 256 grids of fewer than two rounds of 128-row tiles (one work-group
-  // per CU) take the key-split kernel, whose 64-row tiles balance the CUs
+  // d = 32, and d = 256 grids of fewer than two rounds of 128-row tiles (one
+  // work-group per CU), take the key-split kernel, whose 64-row tiles
+  // balance the CUs
+  const dim3 grid_ks(((p.Sq + kTileKs - 1) / kTileKs) * p.Hq * p.B);
   if (d == 32)
-    return launch_kernel(prefill_hd_kernel<32, false>, grid, block, stream, p);
+    return launch_kernel(prefill_hd_ks_kernel<32>, grid_ks, block, stream, p);
   else if (d == 256 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
-    return launch_kernel(prefill_hd_ks_kernel<256>, dim3(((p.Sq + kTileKs - 1) / kTileKs) * p.Hq * p.B), block, stream, p);
+    return launch_kernel(prefill_hd_ks_kernel<256>, grid_ks, block, stream, p);
   else if (d == 256)
     return launch_kernel(prefill_hd_kernel<256, false>, grid, block, stream, p);
   else

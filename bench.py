@@ -322,18 +322,20 @@ def main():
             "note": "chunk of Sq new queries per sequence over its paged cache (chunk included); 100 back-to-back calls"}
 
     def leg_head_dims():
-        """head dims 256 and 96"""
-        # head dims 256 and 96: back-to-back calls, as above
+        """head dims 256, 96 and 32"""
+        # head dims 256, 96 and 32: back-to-back calls, as above
         n_cus = torch.cuda.get_device_properties(0).multi_processor_count
 
         def hd_kernel_name(hc):
-            # d = 256 grids under two rounds of 128-row tiles take the key-split kernel
+            # d = 32, and d = 256 grids under two rounds of 128-row tiles, take the key-split kernel
             tiles = -(-hc.Sq // 128) * hc.Hq * hc.B
             if hc.d == 96:
                 return "prefill_bf16_kernel<96, false>"
+            if hc.d == 32:
+                return "prefill_hd_ks_kernel<32>"
             return "prefill_hd_ks_kernel<256>" if hc.d == 256 and tiles < 2 * n_cus else f"prefill_hd_kernel<{hc.d}>"
         hd = {}
-        for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96()):
+        for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96(), workloads.prefill_gqa_d32()):
             hq_, hk_, hv_ = bf16(hc.q), bf16(hc.k), bf16(hc.v)
             ho = torch.empty_like(hq_)
             hargs = (ctypes.c_void_p(hq_.data_ptr()), ctypes.c_void_p(hk_.data_ptr()), ctypes.c_void_p(hv_.data_ptr()),

@@ -37,8 +37,8 @@ def oracle_out(case):
     return o
 
 
-@pytest.mark.parametrize("make", [workloads.prefill_gqa_d256, workloads.prefill_mha_d96],
-                         ids=["gqa_b1h16x8s2048d256", "mha_b1h32s2048d96"])
+@pytest.mark.parametrize("make", [workloads.prefill_gqa_d256, workloads.prefill_mha_d96, workloads.prefill_gqa_d32],
+                         ids=["gqa_b1h16x8s2048d256", "mha_b1h32s2048d96", "gqa_b1h32x8s2048d32"])
 def test_full_size(make):
     case = make()
     assert_bf16_close(host_f64(run_case(case)), oracle_out(case), case.name)
@@ -60,6 +60,9 @@ SHAPES = [
     (1, 2, 1, 128, 4096, 32, False),     # long KV
     (1, 2, 1, 33, 4000, 256, True),
     (1, 3, 1, 65, 191, 96, False),
+    (2, 4, 1, 65, 300, 32, True),        # d = 32 (key-split kernel): MQA, Sq < Skv
+    (1, 4, 2, 300, 100, 32, False),      # Sq > Skv non-causal
+    (3, 6, 2, 191, 191, 32, True),
     # d = 256 grids of at least two rounds of 128-row tiles (512 on 256 CUs)
     # take the one-group kernel, smaller ones the key-split kernel
     (4, 16, 8, 1024, 1024, 256, True),
@@ -94,7 +97,7 @@ def test_bf16_scale_sign_and_zero(d, scale):
 
 
 @pytest.mark.parametrize("profile", ["rising", "falling"])
-@pytest.mark.parametrize("d", [96, 256])
+@pytest.mark.parametrize("d", [32, 96, 256])
 def test_bf16_score_jumps_between_blocks(profile, d):
     """Key magnitudes ramp along the sequence, so row maxima jump between key
     blocks far beyond the lazy rescale threshold."""
@@ -139,10 +142,11 @@ def test_output_canary_untouched(d):
     assert_bf16_close(host_f64(o), oracle_out(case), case.name)
 
 
-@pytest.mark.parametrize("d,B", [(128, 1), (256, 1), (256, 4), (96, 1)])
+@pytest.mark.parametrize("d,B", [(128, 1), (256, 1), (256, 4), (96, 1), (32, 1)])
 def test_graph_capture_replays(d, B):
-    """fa_prefill captured in a HIP graph (the ping-pong kernel at d = 128, the
-    key-split and one-group kernels at d = 256, the one-group kernel at d = 96):
+    """fa_prefill captured in a HIP graph (the ping-pong kernel at d = 128 and
+    96, the key-split and one-group kernels at d = 256, the key-split kernel at
+    d = 32):
     every replay, with eager work between replays and new q written in place,
     equals the eager call bit for bit."""
     torch = torch_gpu()

@@ -130,6 +130,13 @@ def prefill_mha_d96() -> PrefillCase:
                         name="prefill_mha_b1h32s2048d96")
 
 
+def prefill_gqa_d32() -> PrefillCase:
+    """bf16 GQA causal prefill at head dim 32: the headline prefill's shape
+    (B=1, Hq=32, Hkv=8, Sq=Skv=2048) at d=32, scale 1/sqrt(32)."""
+    return prefill_case(1, 32, 8, 2048, 2048, 32, True, "bf16", seed=1013, scale=1.0 / math.sqrt(32),
+                        name="prefill_gqa_b1h32x8s2048d32")
+
+
 # --------------------------------------------------------------------------- decode
 
 
