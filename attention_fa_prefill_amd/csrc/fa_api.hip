@@ -39,7 +39,7 @@ fa_status check_prefill(const void* q, const void* k, const void* v, void* o, in
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return FA_ERR_ALIGN;
   // the bf16 kernels run one work-group per (pair of 128-row query tiles, or
   // one tile for the other head dims, head, batch)
-  const long tiles = ((long)Sq + 63) / 64;  // (the key-split kernel's 64-row tiles)
+  const long tiles = ((long)Sq + 31) / 32;  // (the key-split kernel's tiles: 32 rows at d = 32)
   if (tiles * Hq * B > (long)INT32_MAX) return FA_ERR_SHAPE;
   return FA_OK;
 }

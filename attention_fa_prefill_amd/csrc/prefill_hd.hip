@@ -26,8 +26,8 @@
 //     MFMA and softmax phases;
 //   - prefill without a cache runs prefill_hd_ks_kernel instead at d = 32,
 //     and at d = 256 on grids of fewer than two rounds of 128-row tiles (one
-//     work-group per CU): 64-row tiles whose keys are split between two wave
-//     pairs (below).
+//     work-group per CU): smaller tiles whose keys are split between two or
+//     four groups of waves (below).
 #include "fa_internal.h"
 
 namespace fa {
@@ -52,9 +52,10 @@ struct HdCfg {
   static constexpr int NI = kKN * RP / 64 / 4;             // direct-to-LDS loads per wave per block
   static constexpr int STAGE = kKN * RP * 8;               // bf16 elements per LDS stage of K or V
   // waves per SIMD the kernels are compiled for: d = 256 needs all registers;
-  // d = 32 fits at four (97 registers in the one-group kernel, 73 in the
-  // key-split one; four work-groups per CU, whose softmax and MFMA phases
-  // overlap: the one-group kernel ran 13 % faster at B = 4 than at two)
+  // d = 32 fits at four (97 registers in the one-group kernel, 71-73 in the
+  // key-split one), so at least four work-groups share a CU and overlap their
+  // softmax and MFMA phases (the one-group kernel ran 13 % faster at B = 4
+  // than at two)
   static constexpr int OCC = D > 128 ? 1 : (D <= 32 ? 4 : 2);
 };
 
@@ -351,35 +352,59 @@ prefill_hd_kernel(PrefillParams p) {
   }
 }
 
-// The keys of each tile split between two wave pairs: a work-group owns a
-// 64-row query tile; waves 2kh and 2kh+1 own its two 32-row halves over the
-// 32-key blocks kh, kh+2, kh+4, ... (kh = 0, 1), and the two partial states of
-// each row are merged through LDS at the end. Against one wave per 32 rows
-// over all keys this halves the longest chain of blocks in a causal grid, and
-// the 64-row tiles (twice as many work-groups, most keys first) balance the
-// CUs: at d = 256 they fill two rounds where 128-row tiles made one
-// unbalanced round. At d = 32 (73 registers, 32 KB, four work-groups per CU)
-// a block's work is short against the latency of its loads, and twice as
-// many independent chains of half the length keep more of them in flight.
-constexpr int kTileKs = 64;  // query rows per work-group
+// The keys of each tile split between KH wave groups (KH = 2 or 4): a
+// work-group of 4 waves owns a 32·(4/KH)-row query tile; wave w owns the
+// 32-row part rh = w mod (4/KH) of it over the 32-key blocks kh, kh+KH,
+// kh+2KH, ... (kh = w div (4/KH)), and the KH partial states of each row are
+// merged through LDS at the end. Against one wave per 32 rows over all keys
+// this divides the longest chain of blocks in a causal grid by KH, and the
+// smaller tiles (more work-groups, most keys first) balance the CUs.
+//   - d = 256 (KH = 2, 64-row tiles): two rounds at one work-group per CU
+//     where 128-row tiles made one unbalanced round.
+//   - d = 32 (4 work-groups per CU): a block's work is short and a wave's
+//     blocks follow each other (load, MFMAs, softmax), so on small causal
+//     grids the longest chains set the time: KH = 4 there, four chains a
+//     quarter as long; elsewhere KH = 2 (fewer merges, more K/V reuse). Its
+//     LDS rows are not padded (64 bytes, 4 chunks): K is swizzled with bits
+//     2-3 of the row, so 16 consecutive rows read one chunk each from 16
+//     distinct 16-byte bank groups, and the V^T transpose reads of 32 lanes
+//     cover 4 whole consecutive rows (256 contiguous bytes) unswizzled.
 constexpr int kKBKs = 32;    // keys per block
 
+template <int D, int KH_>
+struct KsCfg {
+  static constexpr int KH = KH_;                     // key parts
+  static constexpr int RH = 4 / KH;                  // 32-row parts of the tile
+  static constexpr int TILE = 32 * RH;               // query rows per work-group
+  static constexpr int RP = D <= 32 ? HdCfg<D>::CH : HdCfg<D>::RP;  // 16-byte chunks per LDS row
+  static constexpr int STG = kKBKs * RP * 8;         // bf16 elements of one 32-key block
+  static constexpr int NIK = kKBKs * RP / 64 / RH;   // direct-to-LDS loads per wave per block (RH waves share it)
+};
 template <int D>
+__device__ __forceinline__ int ks_swz_k(int row) { return D <= 32 ? (row >> 2) & 3 : hswz_k<D>(row); }
+template <int D>
+__device__ __forceinline__ int ks_swz_v(int row) { return D <= 32 ? 0 : hswz_v<D>(row); }
+
+template <int D, int KH_>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HdCfg<D>::OCC, HdCfg<D>::OCC)))
 prefill_hd_ks_kernel(PrefillParams p) {
   using C = HdCfg<D>;
-  constexpr int STG = kKBKs * C::RP * 8;      // bf16 elements of one 32-key block
-  constexpr int NIK = kKBKs * C::RP / 64 / 2; // direct-to-LDS loads per wave per block (two waves share it)
-  // [stage][key half]; the merge reuses this memory
-  __shared__ __attribute__((aligned(1024))) __bf16 sK[2][2][STG];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV[2][2][STG];
+  using K = KsCfg<D, KH_>;
+  static_assert(KH_ == 2 || KH_ == 4, "two or four key parts");
+  constexpr int KH = K::KH, RH = K::RH, RP = K::RP, STG = K::STG, NIK = K::NIK;
+  static_assert(NIK >= 1 && 64 * NIK * RH == kKBKs * RP, "a block's chunks are split evenly between its waves");
+  static_assert((KH - 1) * C::DB * 4 * 64 * RH * 16 <= 2 * KH * STG * 2, "the merge's partial outputs fit in sK");
+  static_assert((KH - 1) * 128 * RH * 4 <= 2 * KH * STG * 2, "the merge's (m, l) fit in sV");
+  // [stage][key part]; the merge reuses this memory
+  __shared__ __attribute__((aligned(1024))) __bf16 sK[2][KH][STG];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV[2][KH][STG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ln = lane & 31;
-  const int rh = wave & 1, kh = wave >> 1;  // row half, key half
+  const int rh = wave % RH, kh = wave / RH;  // row part, key part
 
-  const int nT = (p.Sq + kTileKs - 1) / kTileKs;
+  const int nT = (p.Sq + K::TILE - 1) / K::TILE;
   int t, h, b;
   {
     const int W = nT * p.Hq * p.B;
@@ -395,22 +420,22 @@ prefill_hd_ks_kernel(PrefillParams p) {
   const int Sq = p.Sq, Skv = p.Skv, off = Skv - Sq;
   const bool causal = p.causal != 0;
   const float c = p.c;
-  const int q_last = min(t * kTileKs + kTileKs, Sq) - 1;
+  const int q_last = min(t * K::TILE + K::TILE, Sq) - 1;
   const int kend = causal ? min(Skv, q_last + off + 1) : Skv;
   const int nb = (kend + kKBKs - 1) / kKBKs;  // 32-key blocks the tile sees
-  const int iters = (nb + 1) / 2;
+  const int iters = (nb + KH - 1) / KH;
 
   const __bf16* kbh = (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
   const __bf16* vbh = (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
   const __bf16* qbh = (const __bf16*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
 
-  // this wave loads rows 16 rh .. 16 rh + 15 of its key half's blocks
+  // this wave loads rows (32 / RH) rh .. (32 / RH) (rh + 1) - 1 of its key part's blocks
   uint32_t koff[NIK], voff[NIK];
 #pragma unroll
   for (int ii = 0; ii < NIK; ++ii) {
     const int P = 64 * (NIK * rh + ii) + lane;
-    const int row = P / C::RP, pc = P % C::RP;
-    const int lk = pc ^ hswz_k<D>(row), lv = pc ^ hswz_v<D>(row);
+    const int row = P / RP, pc = P % RP;
+    const int lk = pc ^ ks_swz_k<D>(row), lv = pc ^ ks_swz_v<D>(row);
     koff[ii] = lk < C::CH ? (uint32_t)(row * D * 2 + lk * 16) : kPadOff;
     voff[ii] = lv < C::CH ? (uint32_t)(row * D * 2 + lv * 16) : kPadOff;
   }
@@ -426,7 +451,7 @@ prefill_hd_ks_kernel(PrefillParams p) {
   };
 
   const uint32_t qflip = p.neg ? 0x80008000u : 0u;
-  const int q0 = t * kTileKs + rh * 32;
+  const int q0 = t * K::TILE + rh * 32;
   const int qrow = q0 + ln;
   bf16x8 qreg[C::KS];
 #pragma unroll
@@ -442,15 +467,15 @@ prefill_hd_ks_kernel(PrefillParams p) {
   for (int db = 0; db < C::DB; ++db) O[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int kr0 = ln * (C::RP * 16);
-  const int sw0 = hswz_k<D>(ln);
+  const int kr0 = ln * (RP * 16);
+  const int sw0 = ks_swz_k<D>(ln);
   const int gg = lane >> 4, jj = lane & 15, dh = gg & 1;
   auto vread = [&](const char* vb, int s, int db) __attribute__((always_inline)) {
     const int row1 = 16 * s + 4 * hl + (jj >> 2);
     const int row2 = row1 + 8;
     const int colb = (32 * db + 16 * dh + 4 * (jj & 3)) * 2;
-    const char* a1 = vb + row1 * (C::RP * 16) + (((colb >> 4) ^ hswz_v<D>(row1)) << 4) + (colb & 15);
-    const char* a2 = vb + row2 * (C::RP * 16) + (((colb >> 4) ^ hswz_v<D>(row2)) << 4) + (colb & 15);
+    const char* a1 = vb + row1 * (RP * 16) + (((colb >> 4) ^ ks_swz_v<D>(row1)) << 4) + (colb & 15);
+    const char* a2 = vb + row2 * (RP * 16) + (((colb >> 4) ^ ks_swz_v<D>(row2)) << 4) + (colb & 15);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a1);
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)a2);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -465,17 +490,16 @@ prefill_hd_ks_kernel(PrefillParams p) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
     __syncthreads();
     const int st = i & 1;
-    const int jn = 2 * (i + 1) + kh;
+    const int jn = KH * (i + 1) + kh;
     if (jn < nb) {
       dma(kbh, sK[st ^ 1][kh], koff, jn);
       dma(vbh, sV[st ^ 1][kh], voff, jn);
     }
-    const int jb = 2 * i + kh;
+    const int jb = KH * i + kh;
     const int kv0 = jb * kKBKs;
     if (jb >= nb || (causal && kv0 > q0 + 31 + off)) continue;
     const char* kb = (const char*)sK[st][kh];
     const char* vb = (const char*)sV[st][kh];
-
     f32x16 S = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
@@ -535,29 +559,45 @@ prefill_hd_ks_kernel(PrefillParams p) {
         O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vb, s, db), P[s], O[db], 0, 0, 0);
   }
 
-  // merge the key halves: the kh = 1 waves hand (m, l, O) to the kh = 0 waves
+  // merge the key parts: the kh > 0 waves hand (m, l, O) to the kh = 0 wave
   // of the same rows through LDS (the stages are free once every wave is here)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  float4* xo = (float4*)&sK[0][0][0] + rh * (C::DB * 4 * 64);  // 32 KB per row half
-  float* xm = (float*)&sV[0][0][0] + rh * 128;
-  if (kh == 1) {
+  float4* xo = (float4*)&sK[0][0][0];  // [key part - 1][row part][db][rg][lane]
+  float* xm = (float*)&sV[0][0][0];    // [key part - 1][row part][m, l][lane]
+  constexpr int XO = RH * C::DB * 4 * 64, XM = RH * 128;
+  if (kh > 0) {
+    float4* xw = xo + (kh - 1) * XO + rh * (C::DB * 4 * 64);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg)
-        xo[(db * 4 + rg) * 64 + lane] =
+        xw[(db * 4 + rg) * 64 + lane] =
             make_float4(O[db][4 * rg], O[db][4 * rg + 1], O[db][4 * rg + 2], O[db][4 * rg + 3]);
-    xm[lane] = m_run;
-    xm[64 + lane] = l_run;
+    float* xmw = xm + (kh - 1) * XM + rh * 128;
+    xmw[lane] = m_run;
+    xmw[64 + lane] = l_run;
   }
   __syncthreads();
   if (kh == 0) {
-    const float m1 = xm[lane], l1 = xm[64 + lane];
-    const float M = fmaxf(m_run, m1);  // finite: every row sees key 0 in block 0
-    const float f0 = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-    const float f1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-    const float lt = hpair_sum(l_run * f0 + l1 * f1);
+    float mk[KH], lk[KH], f[KH];
+    mk[0] = m_run;
+    lk[0] = l_run;
+#pragma unroll
+    for (int u = 1; u < KH; ++u) {
+      mk[u] = xm[(u - 1) * XM + rh * 128 + lane];
+      lk[u] = xm[(u - 1) * XM + rh * 128 + 64 + lane];
+    }
+    float M = mk[0];  // finite: every row sees key 0 in block 0
+#pragma unroll
+    for (int u = 1; u < KH; ++u) M = fmaxf(M, mk[u]);
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < KH; ++u) {
+      f[u] = (mk[u] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mk[u] - M);
+      lsum += lk[u] * f[u];
+    }
+    const float lt = hpair_sum(lsum);
     const float inv = 1.0f / lt;
     if (qrow < Sq) {
       __bf16* dst = (__bf16*)p.o + (((size_t)b * p.Hq + h) * Sq + qrow) * D;
@@ -565,14 +605,19 @@ prefill_hd_ks_kernel(PrefillParams p) {
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          const float4 o1 = xo[(db * 4 + rg) * 64 + lane];
-          const float v0 = (O[db][4 * rg + 0] * f0 + o1.x * f1) * inv;
-          const float v1 = (O[db][4 * rg + 1] * f0 + o1.y * f1) * inv;
-          const float v2 = (O[db][4 * rg + 2] * f0 + o1.z * f1) * inv;
-          const float v3 = (O[db][4 * rg + 3] * f0 + o1.w * f1) * inv;
+          float v0 = O[db][4 * rg + 0] * f[0], v1 = O[db][4 * rg + 1] * f[0];
+          float v2 = O[db][4 * rg + 2] * f[0], v3 = O[db][4 * rg + 3] * f[0];
+#pragma unroll
+          for (int u = 1; u < KH; ++u) {
+            const float4 o1 = xo[(u - 1) * XO + rh * (C::DB * 4 * 64) + (db * 4 + rg) * 64 + lane];
+            v0 += o1.x * f[u];
+            v1 += o1.y * f[u];
+            v2 += o1.z * f[u];
+            v3 += o1.w * f[u];
+          }
           uint2 w;
-          w.x = hpack(v0, v1);
-          w.y = hpack(v2, v3);
+          w.x = hpack(v0 * inv, v1 * inv);
+          w.y = hpack(v2 * inv, v3 * inv);
           *(uint2*)(dst + 32 * db + 8 * rg + 4 * hl) = w;
         }
     }
@@ -600,11 +645,16 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
   // d = 32, and d = 256 grids of fewer than two rounds of 128-row tiles (one
   // work-group per CU), take the key-split kernel, whose 64-row tiles
   // balance the CUs
-  const dim3 grid_ks(((p.Sq + kTileKs - 1) / kTileKs) * p.Hq * p.B);
-  if (d == 32)
-    return launch_kernel(prefill_hd_ks_kernel<32>, grid_ks, block, stream, p);
+  const long tiles64 = (long)((p.Sq + 63) / 64) * p.Hq * p.B;
+  const dim3 grid_ks2(tiles64), grid_ks4(((p.Sq + 31) / 32) * p.Hq * p.B);
+  // d = 32: four key parts on causal grids of at most two rounds of 64-row
+  // tiles (four work-groups per CU), two otherwise
+  if (d == 32 && p.causal && p.cus > 0 && tiles64 <= 8L * p.cus)
+    return launch_kernel(prefill_hd_ks_kernel<32, 4>, grid_ks4, block, stream, p);
+  else if (d == 32)
+    return launch_kernel(prefill_hd_ks_kernel<32, 2>, grid_ks2, block, stream, p);
   else if (d == 256 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
-    return launch_kernel(prefill_hd_ks_kernel<256>, grid_ks, block, stream, p);
+    return launch_kernel(prefill_hd_ks_kernel<256, 2>, grid_ks2, block, stream, p);
   else if (d == 256)
     return launch_kernel(prefill_hd_kernel<256, false>, grid, block, stream, p);
   else

@@ -328,12 +328,14 @@ def main():
 
         def hd_kernel_name(hc):
             # d = 32, and d = 256 grids under two rounds of 128-row tiles, take the key-split kernel
+            # (d = 32: four key parts on causal grids of at most 8 * CUs 64-row tiles, else two)
             tiles = -(-hc.Sq // 128) * hc.Hq * hc.B
             if hc.d == 96:
                 return "prefill_bf16_kernel<96, false>"
             if hc.d == 32:
-                return "prefill_hd_ks_kernel<32>"
-            return "prefill_hd_ks_kernel<256>" if hc.d == 256 and tiles < 2 * n_cus else f"prefill_hd_kernel<{hc.d}>"
+                return "prefill_hd_ks_kernel<32, 4>" if -(-hc.Sq // 64) * hc.Hq * hc.B <= 8 * n_cus else \
+                    "prefill_hd_ks_kernel<32, 2>"
+            return "prefill_hd_ks_kernel<256, 2>" if hc.d == 256 and tiles < 2 * n_cus else f"prefill_hd_kernel<{hc.d}>"
         hd = {}
         for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96(), workloads.prefill_gqa_d32()):
             hq_, hk_, hv_ = bf16(hc.q), bf16(hc.k), bf16(hc.v)
