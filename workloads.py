@@ -90,6 +90,17 @@ class PrefillCase:
         return conv(self.q), conv(self.k), conv(self.v)
 
 
+def device_normal_bf16(shape, seed: int, device="cuda"):
+    """N(0, 1) values rounded to bf16, drawn on the device by torch's seeded
+    generator: inputs too large to build on the host (several GB). Tests copy
+    the slices the oracle needs back to the host."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+
 def prefill_case(B, Hq, Hkv, Sq, Skv, d, causal=True, dtype="bf16", seed=1, scale=None, name=None) -> PrefillCase:
     """q [B,Hq,Sq,d], k/v [B,Hkv,Skv,d], i.i.d. N(0,1) from (seed, stream 0/1/2)."""
     if scale is None:
