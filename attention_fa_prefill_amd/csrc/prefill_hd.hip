@@ -515,22 +515,43 @@ prefill_hd_ks_kernel(PrefillParams p) {
       for (int r = 0; r < 16; ++r)
         if (8 * (r >> 2) + (r & 3) > lim) S[r] = -INFINITY;
     }
-    float mx = S[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
-    mx = hpair_max(mx);
-    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+    // The block is exponentiated against the current reference without a
+    // max search; the block's maximum is taken (and the reference raised when
+    // it grows by more than kTau) only when a row has no reference yet, or
+    // when a lane's partial block sum passes 2^16 (which also catches inf and
+    // NaN). Probabilities therefore stay at most 2^16.
     float alpha = 1.f;
-    if (cand > m_run + kTau) {
-      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
-      m_run = cand;
-    }
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
     float e[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c, -mu));
-    bf16x8 P[2];
     float la = 0.f, lb = 0.f;
+    auto exponentiate = [&](float mu) __attribute__((always_inline)) {
+      la = 0.f;
+      lb = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c, -mu));
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        la += e[r];
+        lb += e[r + 1];
+      }
+    };
+    bool redo = __any(m_run == -INFINITY);
+    if (!redo) {
+      exponentiate(m_run);
+      redo = __any(!(la + lb <= 65536.f));
+    }
+    if (redo) {
+      float mx = S[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, S[r]);
+      mx = hpair_max(mx);
+      const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+      if (cand > m_run + kTau) {
+        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
+        m_run = cand;
+      }
+      exponentiate((m_run == -INFINITY) ? 0.f : m_run);
+    }
+    bf16x8 P[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       uint4 w;
@@ -539,11 +560,6 @@ prefill_hd_ks_kernel(PrefillParams p) {
       w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
       w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
       P[s] = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-      for (int r = 0; r < 8; r += 2) {
-        la += e[8 * s + r];
-        lb += e[8 * s + r + 1];
-      }
     }
     l_run = alpha * l_run + (la + lb);
     if (__any(alpha != 1.f)) {

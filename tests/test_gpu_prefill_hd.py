@@ -63,6 +63,7 @@ SHAPES = [
     (2, 4, 1, 65, 300, 32, True),        # d = 32 (key-split kernel): MQA, Sq < Skv
     (1, 4, 2, 300, 100, 32, False),      # Sq > Skv non-causal
     (3, 6, 2, 191, 191, 32, True),
+    (2, 64, 8, 1100, 1100, 32, True),    # a causal grid past two rounds: two key parts
     # d = 256 grids of at least two rounds of 128-row tiles (512 on 256 CUs)
     # take the one-group kernel, smaller ones the key-split kernel
     (4, 16, 8, 1024, 1024, 256, True),
