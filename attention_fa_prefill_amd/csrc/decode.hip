@@ -10,7 +10,9 @@
 //
 // Split kernel: one work-group (4 waves) per (sequence b, kv head g, group of
 // up to 16 query heads sharing g, split s of T tokens), live splits numbered
-// densely so that the XCDs get equal shares of a mixed-length batch. T is the
+// densely so that the XCDs get equal shares of a mixed-length batch (a single
+// sequence whose splits fit one round is numbered in order, and its
+// work-groups read their block-table entries beside its length). T is the
 // caller's split size, or with the default one of a few sizes chosen from
 // seqlens on the device, so that the live splits fill whole rounds of
 // resident work-groups. Waves take 32-token
@@ -27,7 +29,7 @@
 // Every load goes through a buffer resource whose record count ends at the
 // last valid token row of its page, so rows past the sequence length (and the
 // slack of the last page) read as zero without touching memory; their scores
-// are set to -inf. Block-table entries past the last page are never read.
+// are set to -inf. Block-table entries past the last page are never used.
 // At the end the 4 waves' states are merged in LDS and the split writes its
 // normalised output and natural-log log-sum-exp to the workspace.
 //
