@@ -361,10 +361,10 @@ prefill_hd_kernel(PrefillParams p) {
 // smaller tiles (more work-groups, most keys first) balance the CUs.
 //   - d = 256 (KH = 2, 64-row tiles): two rounds at one work-group per CU
 //     where 128-row tiles made one unbalanced round.
-//   - d = 32 (4 work-groups per CU): a block's work is short and a wave's
-//     blocks follow each other (load, MFMAs, softmax), so on small causal
-//     grids the longest chains set the time: KH = 4 there, four chains a
-//     quarter as long; elsewhere KH = 2 (fewer merges, more K/V reuse). Its
+//   - d = 32 (four or more work-groups per CU): a block's work is short and
+//     a wave's blocks follow each other (load, MFMAs, softmax), so on small
+//     causal grids the longest chains set the time: KH = 4 there, four chains
+//     a quarter as long; elsewhere KH = 2 (fewer merges, more K/V reuse). Its
 //     LDS rows are not padded (64 bytes, 4 chunks): K is swizzled with bits
 //     2-3 of the row, so 16 consecutive rows read one chunk each from 16
 //     distinct 16-byte bank groups, and the V^T transpose reads of 32 lanes
