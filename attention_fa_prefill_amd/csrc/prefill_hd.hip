@@ -283,38 +283,91 @@ prefill_hd_kernel(PrefillParams p) {
         if (ko + 32 > lim) S1[r] = -INFINITY;
       }
     }
-    // running reference: raised to the block's scaled row maximum when that
-    // exceeds it by more than kTau, so every probability stays <= 2^kTau
-    float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-    mx = hpair_max(mx);
-    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+    // d = 32 (the vector work per MFMA is largest): exponent reference as in
+    // the key-split kernel below (on the chunked prefill workload 351 -> 325
+    // us); d = 256 keeps the block maximum of every block (the lazy form was
+    // 2-3 % slower there)
     float alpha = 1.f;
-    if (cand > m_run + kTau) {
-      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
-      m_run = cand;
-    }
-    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
     bf16x8 P[2][2];
     float la = 0.f, lb = 0.f;
+    if constexpr (D <= 32) {
+      // Exponent reference, as in the key-split kernel below: the block is
+      // exponentiated against the current reference without a max search; the
+      // block's maximum is taken (and the reference raised when it grows by more
+      // than kTau) only when a row has no reference yet, or when a lane's
+      // partial block sum passes 2^16 (which also catches inf and NaN).
+      auto exponentiate = [&](float mu) __attribute__((always_inline)) {
+        la = 0.f;
+        lb = 0.f;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      float e[16];
+        for (int sub = 0; sub < 2; ++sub) {
+          float e[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sub ? S1[r] : S0[r], c, -mu));
+          for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sub ? S1[r] : S0[r], c, -mu));
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        uint4 w;
-        w.x = hpack(e[8 * s + 0], e[8 * s + 1]);
-        w.y = hpack(e[8 * s + 2], e[8 * s + 3]);
-        w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
-        w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
-        P[sub][s] = __builtin_bit_cast(bf16x8, w);
+          for (int s = 0; s < 2; ++s) {
+            uint4 w;
+            w.x = hpack(e[8 * s + 0], e[8 * s + 1]);
+            w.y = hpack(e[8 * s + 2], e[8 * s + 3]);
+            w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
+            w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
+            P[sub][s] = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-        for (int r = 0; r < 8; r += 2) {
-          la += e[8 * s + r];
-          lb += e[8 * s + r + 1];
+            for (int r = 0; r < 8; r += 2) {
+              la += e[8 * s + r];
+              lb += e[8 * s + r + 1];
+            }
+          }
+        }
+      };
+      bool redo = __any(m_run == -INFINITY);
+      if (!redo) {
+        exponentiate(m_run);
+        redo = __any(!(la + lb <= 65536.f));
+      }
+      if (redo) {
+        float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+        mx = hpair_max(mx);
+        const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+        if (cand > m_run + kTau) {
+          alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
+          m_run = cand;
+        }
+        exponentiate((m_run == -INFINITY) ? 0.f : m_run);
+      }
+    } else {
+      // running reference: raised to the block's scaled row maximum when that
+      // exceeds it by more than kTau, so every probability stays <= 2^kTau
+      float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+      mx = hpair_max(mx);
+      const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
+      if (cand > m_run + kTau) {
+        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
+        m_run = cand;
+      }
+      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        float e[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sub ? S1[r] : S0[r], c, -mu));
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          uint4 w;
+          w.x = hpack(e[8 * s + 0], e[8 * s + 1]);
+          w.y = hpack(e[8 * s + 2], e[8 * s + 3]);
+          w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
+          w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
+          P[sub][s] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+          for (int r = 0; r < 8; r += 2) {
+            la += e[8 * s + r];
+            lb += e[8 * s + r + 1];
+          }
         }
       }
     }
