@@ -149,8 +149,8 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
   if (!aligned4(seqlens) || (block_table && !aligned4(block_table))) return FA_ERR_ALIGN;
   if (!block_table && (size_t)B * (size_t)max_kv_len > (size_t)INT32_MAX) return FA_ERR_SHAPE;
   // one work-group per (query tile, head, sequence), padded to whole rounds of
-  // (sequence, kv head) groups on the 8 XCDs
-  const long tiles = ((long)Sq + 127) / 128;
+  // (sequence, kv head) groups on the 8 XCDs (tiles of 32 rows at the least)
+  const long tiles = ((long)Sq + 31) / 32;
   if (8 * (((long)B * Hkv + 7) / 8) * (Hq / Hkv) * tiles > (long)INT32_MAX) return FA_ERR_SHAPE;
   fa::PrefillParams p = make_prefill(q, kcache, vcache, o, B, Hq, Hkv, Sq, max_kv_len, scale, causal);
   p.lens = seqlens;
@@ -158,6 +158,7 @@ fa_status fa_prefill_cache(const void* q, const void* kcache, const void* vcache
   p.max_len = max_kv_len;
   p.pps = (max_kv_len + 15) / 16;
   if (d == 64 || d == 96 || d == 128) return from_hip(fa::launch_prefill_bf16(p, d, (hipStream_t)stream));
+  p.cus = resident_split_groups() / 2;
   return from_hip(fa::launch_prefill_hd(p, d, (hipStream_t)stream));
 }
 

@@ -22,12 +22,12 @@
 //     padding chunks are filled with zeros by out-of-range buffer loads;
 //   - d = 256 needs O^T (128 registers) and Q^T (64) per wave, so it runs one
 //     wave per SIMD with up to 512 registers and 128 KB of LDS per work-group;
-//     d = 32 runs four work-groups per CU, whose waves overlap each other's
-//     MFMA and softmax phases;
-//   - prefill without a cache runs prefill_hd_ks_kernel instead at d = 32,
-//     and at d = 256 on grids of fewer than two rounds of 128-row tiles (one
-//     work-group per CU): smaller tiles whose keys are split between two or
-//     four groups of waves (below).
+//   - d = 32 (with or without a cache), and d = 256 prefill without a cache
+//     on grids of fewer than two rounds of 128-row tiles (one work-group per
+//     CU), run prefill_hd_ks_kernel instead: smaller tiles whose keys are
+//     split between two or four groups of waves (below); at d = 32 four or
+//     more of its work-groups share a CU and overlap their waves' MFMA and
+//     softmax phases.
 #include "fa_internal.h"
 
 namespace fa {
@@ -52,10 +52,8 @@ struct HdCfg {
   static constexpr int NI = kKN * RP / 64 / 4;             // direct-to-LDS loads per wave per block
   static constexpr int STAGE = kKN * RP * 8;               // bf16 elements per LDS stage of K or V
   // waves per SIMD the kernels are compiled for: d = 256 needs all registers;
-  // d = 32 fits at four (97 registers in the one-group kernel, 71-73 in the
-  // key-split one), so at least four work-groups share a CU and overlap their
-  // softmax and MFMA phases (the one-group kernel ran 13 % faster at B = 4
-  // than at two)
+  // the d = 32 key-split kernel fits at four (80-82 registers), so at least
+  // four work-groups share a CU and overlap their softmax and MFMA phases
   static constexpr int OCC = D > 128 ? 1 : (D <= 32 ? 4 : 2);
 };
 
@@ -90,6 +88,45 @@ __device__ __forceinline__ uint32_t hpack(float a, float b) {
 // cached tokens (bottom-right causal alignment); a row with no visible key
 // gives zeros. Each wave's loads of a 64-key block cover exactly its 16 rows,
 // one page, read through one buffer resource bounded at the last valid key.
+// Chunked prefill work order: a tile's cost is its sequence's cached length.
+// The (sequence, kv head) groups are ordered by descending length and dealt
+// whole, round-robin, to the 8 XCDs (each XCD gets an equal mix of long and
+// short sequences, longest first, and keeps a kv head's K/V in one L2);
+// inside a group, tiles by descending causal cost (nT tiles), then heads.
+// Returns false for a work-group past its XCD's groups (uniform). Every
+// thread of the work-group calls it (it synchronises when it ranks the
+// lengths); `slot` is an int of LDS not yet in use.
+__device__ __forceinline__ bool ranked_cache_item(const PrefillParams& p, int nT, int tid, int* slot, int& b, int& h,
+                                                  int& t) {
+  const int G = p.Hq / p.Hkv;
+  const int per_group = G * nT;
+  const int xcd = (int)blockIdx.x % kXcdsHd, idx = (int)blockIdx.x / kXcdsHd;
+  const int k = xcd + kXcdsHd * (idx / per_group);
+  if (k >= p.B * p.Hkv) return false;
+  const int within = idx % per_group;
+  const int r = k / p.Hkv;
+  h = (k % p.Hkv) * G + within % G;
+  t = nT - 1 - within / G;
+  // the sequence of length rank r (longest first, ties by index); beyond
+  // kRankMaxBHd sequences, index order
+  b = r;
+  if (p.B <= kRankMaxBHd) {
+    for (int u0 = tid; u0 < p.B; u0 += 256) {
+      const int lt = min(max(p.lens[u0], 0), p.max_len);
+      int rank = 0;
+      for (int u = 0; u < p.B; ++u) {
+        const int lu = min(max(p.lens[u], 0), p.max_len);
+        rank += (lu > lt || (lu == lt && u < u0)) ? 1 : 0;
+      }
+      if (rank == r) *slot = u0;
+    }
+    __syncthreads();
+    b = __builtin_amdgcn_readfirstlane(*slot);
+    __syncthreads();  // every wave has read the slot before its memory is reused
+  }
+  return true;
+}
+
 template <int D, bool CACHE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HdCfg<D>::OCC, HdCfg<D>::OCC)))
 prefill_hd_kernel(PrefillParams p) {
@@ -107,42 +144,9 @@ prefill_hd_kernel(PrefillParams p) {
   // query head, then sequence; each XCD takes a contiguous range of items,
   // so the query heads of one kv head share that XCD's L2.
   int t, h, b;
-  if constexpr (CACHE && C::OCC > 1) {
-    // With a cache a tile's cost is its sequence's cached length. The
-    // (sequence, kv head) groups are ordered by descending length and dealt
-    // whole, round-robin, to the 8 XCDs (each XCD gets an equal mix of long
-    // and short sequences, longest first, and keeps a kv head's K/V in one
-    // L2); inside a group, tiles by descending causal cost, then heads.
-    // (d = 256, one work-group per CU, keeps the plain order below: measured
-    // faster there on mixed lengths.)
-    const int G = p.Hq / p.Hkv;
-    const int per_group = G * p.nT;
-    const int xcd = (int)blockIdx.x % kXcdsHd, idx = (int)blockIdx.x / kXcdsHd;
-    const int k = xcd + kXcdsHd * (idx / per_group);
-    if (k >= p.B * p.Hkv) return;  // past this XCD's groups (uniform)
-    const int within = idx % per_group;
-    const int r = k / p.Hkv;
-    h = (k % p.Hkv) * G + within % G;
-    t = p.nT - 1 - within / G;
-    // the sequence of length rank r (longest first, ties by index); beyond
-    // kRankMaxBHd sequences, index order
-    b = r;
-    if (p.B <= kRankMaxBHd) {
-      int* rank_slot = (int*)sK0;  // not in use yet
-      for (int u0 = tid; u0 < p.B; u0 += 256) {
-        const int lt = min(max(p.lens[u0], 0), p.max_len);
-        int rank = 0;
-        for (int u = 0; u < p.B; ++u) {
-          const int lu = min(max(p.lens[u], 0), p.max_len);
-          rank += (lu > lt || (lu == lt && u < u0)) ? 1 : 0;
-        }
-        if (rank == r) *rank_slot = u0;
-      }
-      __syncthreads();
-      b = __builtin_amdgcn_readfirstlane(*rank_slot);
-      __syncthreads();  // every wave has read the slot before sK0 is loaded
-    }
-  } else {
+  {
+    // (with a cache too: at d = 256, one work-group per CU, this order measured
+    // faster than the longest-first one on mixed lengths)
     const int W = p.nT * p.Hq * p.B;
     const int L = blockIdx.x;
     const int xcd = L % kXcdsHd, idx = L / kXcdsHd;
@@ -283,91 +287,38 @@ prefill_hd_kernel(PrefillParams p) {
         if (ko + 32 > lim) S1[r] = -INFINITY;
       }
     }
-    // d = 32 (the vector work per MFMA is largest): exponent reference as in
-    // the key-split kernel below (on the chunked prefill workload 351 -> 325
-    // us); d = 256 keeps the block maximum of every block (the lazy form was
-    // 2-3 % slower there)
+    // running reference: raised to the block's scaled row maximum when that
+    // exceeds it by more than kTau, so every probability stays <= 2^kTau
+    float mx = fmaxf(S0[0], S1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
+    mx = hpair_max(mx);
+    const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
     float alpha = 1.f;
+    if (cand > m_run + kTau) {
+      alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
+      m_run = cand;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
     bf16x8 P[2][2];
     float la = 0.f, lb = 0.f;
-    if constexpr (D <= 32) {
-      // Exponent reference, as in the key-split kernel below: the block is
-      // exponentiated against the current reference without a max search; the
-      // block's maximum is taken (and the reference raised when it grows by more
-      // than kTau) only when a row has no reference yet, or when a lane's
-      // partial block sum passes 2^16 (which also catches inf and NaN).
-      auto exponentiate = [&](float mu) __attribute__((always_inline)) {
-        la = 0.f;
-        lb = 0.f;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-          float e[16];
+    for (int sub = 0; sub < 2; ++sub) {
+      float e[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sub ? S1[r] : S0[r], c, -mu));
+      for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sub ? S1[r] : S0[r], c, -mu));
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            uint4 w;
-            w.x = hpack(e[8 * s + 0], e[8 * s + 1]);
-            w.y = hpack(e[8 * s + 2], e[8 * s + 3]);
-            w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
-            w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
-            P[sub][s] = __builtin_bit_cast(bf16x8, w);
+      for (int s = 0; s < 2; ++s) {
+        uint4 w;
+        w.x = hpack(e[8 * s + 0], e[8 * s + 1]);
+        w.y = hpack(e[8 * s + 2], e[8 * s + 3]);
+        w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
+        w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
+        P[sub][s] = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
-            for (int r = 0; r < 8; r += 2) {
-              la += e[8 * s + r];
-              lb += e[8 * s + r + 1];
-            }
-          }
-        }
-      };
-      bool redo = __any(m_run == -INFINITY);
-      if (!redo) {
-        exponentiate(m_run);
-        redo = __any(!(la + lb <= 65536.f));
-      }
-      if (redo) {
-        float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-        mx = hpair_max(mx);
-        const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
-        if (cand > m_run + kTau) {
-          alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
-          m_run = cand;
-        }
-        exponentiate((m_run == -INFINITY) ? 0.f : m_run);
-      }
-    } else {
-      // running reference: raised to the block's scaled row maximum when that
-      // exceeds it by more than kTau, so every probability stays <= 2^kTau
-      float mx = fmaxf(S0[0], S1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(S0[r], S1[r]));
-      mx = hpair_max(mx);
-      const float cand = (mx == -INFINITY) ? -INFINITY : c * mx;
-      if (cand > m_run + kTau) {
-        alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - cand);
-        m_run = cand;
-      }
-      const float mu = (m_run == -INFINITY) ? 0.f : m_run;
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        float e[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = __builtin_amdgcn_exp2f(fmaf(sub ? S1[r] : S0[r], c, -mu));
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          uint4 w;
-          w.x = hpack(e[8 * s + 0], e[8 * s + 1]);
-          w.y = hpack(e[8 * s + 2], e[8 * s + 3]);
-          w.z = hpack(e[8 * s + 4], e[8 * s + 5]);
-          w.w = hpack(e[8 * s + 6], e[8 * s + 7]);
-          P[sub][s] = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-          for (int r = 0; r < 8; r += 2) {
-            la += e[8 * s + r];
-            lb += e[8 * s + r + 1];
-          }
+        for (int r = 0; r < 8; r += 2) {
+          la += e[8 * s + r];
+          lb += e[8 * s + r + 1];
         }
       }
     }
@@ -414,10 +365,11 @@ prefill_hd_kernel(PrefillParams p) {
 // smaller tiles (more work-groups, most keys first) balance the CUs.
 //   - d = 256 (KH = 2, 64-row tiles): two rounds at one work-group per CU
 //     where 128-row tiles made one unbalanced round.
-//   - d = 32 (four or more work-groups per CU): a block's work is short and
-//     a wave's blocks follow each other (load, MFMAs, softmax), so on small
-//     causal grids the longest chains set the time: KH = 4 there, four chains
-//     a quarter as long; elsewhere KH = 2 (fewer merges, more K/V reuse). Its
+//   - d = 32 (four or more work-groups per CU; also the chunked prefill over a
+//     KV cache, CACHE): a block's work is short and a wave's blocks follow
+//     each other (load, MFMAs, softmax), so on small causal grids the longest
+//     chains set the time: KH = 4 there, four chains a quarter as long;
+//     elsewhere KH = 2 (fewer merges, more K/V reuse). Its
 //     LDS rows are not padded (64 bytes, 4 chunks): K is swizzled with bits
 //     2-3 of the row, so 16 consecutive rows read one chunk each from 16
 //     distinct 16-byte bank groups, and the V^T transpose reads of 32 lanes
@@ -438,7 +390,7 @@ __device__ __forceinline__ int ks_swz_k(int row) { return D <= 32 ? (row >> 2) &
 template <int D>
 __device__ __forceinline__ int ks_swz_v(int row) { return D <= 32 ? 0 : hswz_v<D>(row); }
 
-template <int D, int KH_>
+template <int D, int KH_, bool CACHE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HdCfg<D>::OCC, HdCfg<D>::OCC)))
 prefill_hd_ks_kernel(PrefillParams p) {
   using C = HdCfg<D>;
@@ -459,7 +411,9 @@ prefill_hd_ks_kernel(PrefillParams p) {
 
   const int nT = (p.Sq + K::TILE - 1) / K::TILE;
   int t, h, b;
-  {
+  if constexpr (CACHE) {
+    if (!ranked_cache_item(p, nT, tid, (int*)&sK[0][0][0], b, h, t)) return;
+  } else {
     const int W = nT * p.Hq * p.B;
     const int L = blockIdx.x;
     const int xcd = L % kXcdsHd, idx = L / kXcdsHd;
@@ -470,37 +424,69 @@ prefill_hd_ks_kernel(PrefillParams p) {
     b = I / (nT * p.Hq);
   }
   const int g = (int)((long)h * p.Hkv / p.Hq);
-  const int Sq = p.Sq, Skv = p.Skv, off = Skv - Sq;
+  const int Sq = p.Sq;
+  const int Skv = CACHE ? min(max(p.lens[b], 0), p.max_len) : p.Skv;
+  const int off = Skv - Sq;
   const bool causal = p.causal != 0;
   const float c = p.c;
   const int q_last = min(t * K::TILE + K::TILE, Sq) - 1;
-  const int kend = causal ? min(Skv, q_last + off + 1) : Skv;
-  const int nb = (kend + kKBKs - 1) / kKBKs;  // 32-key blocks the tile sees
+  const int kend = causal ? min(Skv, q_last + off + 1) : Skv;  // (CACHE: maybe none)
+  const int nb = max(0, (kend + kKBKs - 1) / kKBKs);  // 32-key blocks the tile sees
   const int iters = (nb + KH - 1) / KH;
 
-  const __bf16* kbh = (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
-  const __bf16* vbh = (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* kbh = CACHE ? (const __bf16*)p.k : (const __bf16*)p.k + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const __bf16* vbh = CACHE ? (const __bf16*)p.v : (const __bf16*)p.v + ((size_t)b * p.Hkv + g) * (size_t)Skv * D;
+  const uint32_t rowstride = CACHE ? (uint32_t)p.Hkv * D * 2u : (uint32_t)D * 2u;
   const __bf16* qbh = (const __bf16*)p.q + ((size_t)b * p.Hq + h) * (size_t)Sq * D;
 
   // this wave loads rows (32 / RH) rh .. (32 / RH) (rh + 1) - 1 of its key part's blocks
+  // (CACHE: offsets relative to the first row of the row's page of 16)
   uint32_t koff[NIK], voff[NIK];
 #pragma unroll
   for (int ii = 0; ii < NIK; ++ii) {
     const int P = 64 * (NIK * rh + ii) + lane;
     const int row = P / RP, pc = P % RP;
     const int lk = pc ^ ks_swz_k<D>(row), lv = pc ^ ks_swz_v<D>(row);
-    koff[ii] = lk < C::CH ? (uint32_t)(row * D * 2 + lk * 16) : kPadOff;
-    voff[ii] = lv < C::CH ? (uint32_t)(row * D * 2 + lv * 16) : kPadOff;
+    const uint32_t rb = (uint32_t)(CACHE ? (row & 15) : row) * rowstride;
+    koff[ii] = lk < C::CH ? rb + (uint32_t)(lk * 16) : kPadOff;
+    voff[ii] = lv < C::CH ? rb + (uint32_t)(lv * 16) : kPadOff;
   }
   auto dma = [&](const __bf16* src, __bf16* stage, const uint32_t* offs, int jb) __attribute__((always_inline)) {
     const int kv0 = jb * kKBKs;
-    const int rows = min(kKBKs, Skv - kv0);
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kRsrcW3);
+    if constexpr (CACHE) {
+      // a load covers RPL rows, LPP loads one page of 16: one buffer
+      // resource per page, its record count ending after the last key that
+      // exists (rows past it read as zero; a page past the sequence is
+      // neither looked up in the block table nor read)
+      constexpr int RPL = 64 / RP, LPP = 16 / RPL;
+      static_assert(RPL <= 16 && NIK % LPP == 0, "a wave's loads cover whole pages");
 #pragma unroll
-    for (int ii = 0; ii < NIK; ++ii)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + 64 * (NIK * rh + ii) * 8), 16,
-                                               (int)offs[ii], 0, 0, 0);
+      for (int pg = 0; pg < NIK / LPP; ++pg) {
+        const int r0 = kv0 + RPL * (NIK * rh + pg * LPP);  // first row of the page
+        const int nvalid = max(0, min(16, Skv - r0));
+        const char* base = (const char*)src;
+        if (nvalid > 0) {
+          const long prow = p.bt ? (long)p.bt[(size_t)b * p.pps + r0 / 16] * 16 : (long)b * p.max_len + r0;
+          base += ((size_t)prow * p.Hkv + g) * (size_t)(D * 2);
+        }
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)base, (short)0, nvalid > 0 ? (nvalid - 1) * (int)rowstride + D * 2 : 0, kRsrcW3);
+#pragma unroll
+        for (int jj = 0; jj < LPP; ++jj) {
+          const int ii = pg * LPP + jj;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + 64 * (NIK * rh + ii) * 8), 16,
+                                                   (int)offs[ii], 0, 0, 0);
+        }
+      }
+    } else {
+      const int rows = min(kKBKs, Skv - kv0);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(src + (size_t)kv0 * D), (short)0, rows * D * 2, kRsrcW3);
+#pragma unroll
+      for (int ii = 0; ii < NIK; ++ii)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(stage + 64 * (NIK * rh + ii) * 8), 16,
+                                                 (int)offs[ii], 0, 0, 0);
+    }
   };
 
   const uint32_t qflip = p.neg ? 0x80008000u : 0u;
@@ -657,7 +643,7 @@ prefill_hd_ks_kernel(PrefillParams p) {
       mk[u] = xm[(u - 1) * XM + rh * 128 + lane];
       lk[u] = xm[(u - 1) * XM + rh * 128 + 64 + lane];
     }
-    float M = mk[0];  // finite: every row sees key 0 in block 0
+    float M = mk[0];  // finite unless the row sees no key (CACHE, Skv < Sq)
 #pragma unroll
     for (int u = 1; u < KH; ++u) M = fmaxf(M, mk[u]);
     float lsum = 0.f;
@@ -667,7 +653,8 @@ prefill_hd_ks_kernel(PrefillParams p) {
       lsum += lk[u] * f[u];
     }
     const float lt = hpair_sum(lsum);
-    const float inv = 1.0f / lt;
+    // (CACHE: a row with no visible key has l = 0 and gives zeros)
+    const float inv = CACHE ? (lt > 0.f ? 1.0f / lt : 0.f) : 1.0f / lt;
     if (qrow < Sq) {
       __bf16* dst = (__bf16*)p.o + (((size_t)b * p.Hq + h) * Sq + qrow) * D;
 #pragma unroll
@@ -698,14 +685,17 @@ prefill_hd_ks_kernel(PrefillParams p) {
 hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) {
   const dim3 grid(p.nT * p.Hq * p.B), block(256);
   if (p.lens) {
-    // chunked prefill over a KV cache: the one-group kernel, one work-group
-    // per (query tile, head, sequence), padded to whole rounds of (sequence,
-    // kv head) groups on the 8 XCDs
-    // (d = 32: padded to whole rounds of (sequence, kv head) groups on the
-    // 8 XCDs, longest sequences first; d = 256: the plain grid)
-    const dim3 grid_c(kXcdsHd * ((p.B * p.Hkv + kXcdsHd - 1) / kXcdsHd) * (p.Hq / p.Hkv) * p.nT);
-    if (d == 32)
-      return launch_kernel(prefill_hd_kernel<32, true>, grid_c, block, stream, p);
+    // chunked prefill over a KV cache: at d = 32 the key-split kernel, one
+    // work-group per (query tile, head, sequence), padded to whole rounds of
+    // (sequence, kv head) groups on the 8 XCDs, longest sequences first; at
+    // d = 256 the one-group kernel in the plain order (the key-split kernel
+    // measured 1-2 % slower there)
+    const long groups = (long)kXcdsHd * ((p.B * p.Hkv + kXcdsHd - 1) / kXcdsHd) * (p.Hq / p.Hkv);
+    const long tiles64c = (long)((p.Sq + 63) / 64) * p.Hq * p.B;
+    if (d == 32 && p.causal && p.cus > 0 && tiles64c <= 8L * p.cus)
+      return launch_kernel(prefill_hd_ks_kernel<32, 4, true>, dim3(groups * ((p.Sq + 31) / 32)), block, stream, p);
+    else if (d == 32)
+      return launch_kernel(prefill_hd_ks_kernel<32, 2, true>, dim3(groups * ((p.Sq + 63) / 64)), block, stream, p);
     else if (d == 256)
       return launch_kernel(prefill_hd_kernel<256, true>, grid, block, stream, p);
     else
@@ -719,11 +709,11 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
   // d = 32: four key parts on causal grids of at most two rounds of 64-row
   // tiles (four work-groups per CU), two otherwise
   if (d == 32 && p.causal && p.cus > 0 && tiles64 <= 8L * p.cus)
-    return launch_kernel(prefill_hd_ks_kernel<32, 4>, grid_ks4, block, stream, p);
+    return launch_kernel(prefill_hd_ks_kernel<32, 4, false>, grid_ks4, block, stream, p);
   else if (d == 32)
-    return launch_kernel(prefill_hd_ks_kernel<32, 2>, grid_ks2, block, stream, p);
+    return launch_kernel(prefill_hd_ks_kernel<32, 2, false>, grid_ks2, block, stream, p);
   else if (d == 256 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
-    return launch_kernel(prefill_hd_ks_kernel<256, 2>, grid_ks2, block, stream, p);
+    return launch_kernel(prefill_hd_ks_kernel<256, 2, false>, grid_ks2, block, stream, p);
   else if (d == 256)
     return launch_kernel(prefill_hd_kernel<256, false>, grid, block, stream, p);
   else
