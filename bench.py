@@ -333,9 +333,10 @@ def main():
             if hc.d == 96:
                 return "prefill_bf16_kernel<96, false>"
             if hc.d == 32:
-                return "prefill_hd_ks_kernel<32, 4>" if -(-hc.Sq // 64) * hc.Hq * hc.B <= 8 * n_cus else \
-                    "prefill_hd_ks_kernel<32, 2>"
-            return "prefill_hd_ks_kernel<256, 2>" if hc.d == 256 and tiles < 2 * n_cus else f"prefill_hd_kernel<{hc.d}>"
+                return "prefill_hd_ks_kernel<32, 4, false>" if -(-hc.Sq // 64) * hc.Hq * hc.B <= 8 * n_cus else \
+                    "prefill_hd_ks_kernel<32, 2, false>"
+            return ("prefill_hd_ks_kernel<256, 2, false>" if hc.d == 256 and tiles < 2 * n_cus
+                    else f"prefill_hd_kernel<{hc.d}, false>")
         hd = {}
         for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96(), workloads.prefill_gqa_d32()):
             hq_, hk_, hv_ = bf16(hc.q), bf16(hc.k), bf16(hc.v)
