@@ -15,9 +15,12 @@ Also reported on the same JSON line:
     on the current kernel source, else null;
   - decode: contiguous 32k (B=4), paged mixed lengths (B=8) and long-context
     256k (B=1), over bf16, FP8 E4M3 and int8 caches: us/call (both kernels)
-    and algorithmic HBM GB/s against 8 TB/s,
-    each call timed alone after a 1 GiB read that evicts the 256 MB
-    last-level cache (a read leaves no dirty lines behind);
+    and algorithmic HBM GB/s against 8 TB/s, two ways: each call timed alone
+    after a 1 GiB read that evicts the 256 MB last-level cache (a read leaves
+    no dirty lines behind), and sustained (calls back to back between one
+    event pair, rotating over copies of the cache that hold at least 768 MiB
+    together, so the cache comes from HBM); the decode roofline takes the
+    sustained figure and shows the isolated one beside it;
   - us/call at B=1 for the fp32 single-head prefill and the bf16 prefill;
   - launch modes for the fp32 single-head prefill and the long-context decode:
     eager isolated, eager back-to-back and HIP-graph replay us/call;
@@ -266,6 +269,30 @@ def main():
             t = timed_calls(dcall, args.decode_reps, evict=True)
             t_warm = timed_calls(dcall, 20, evict=False)
             nbytes = decode_bytes(dc)
+            # Sustained rate, as a serving loop issues decode steps: calls back
+            # to back between one event pair, rotating over copies of the cache
+            # that together hold at least 768 MiB (three times the 256 MB
+            # last-level cache), so that every call reads a cache the previous
+            # calls have pushed out of it.
+            cache_bytes = dk.numel() * dk.element_size() + dv.numel() * dv.element_size()
+            n_copy = max(2, -(-(768 << 20) // cache_bytes))
+            copies = [(dk, dv)] + [(dk.clone(), dv.clone()) for _ in range(n_copy - 1)]
+            rot = [dargs[:1] + (ctypes.c_void_p(ck.data_ptr()), ctypes.c_void_p(cv.data_ptr())) + dargs[3:]
+                   for ck, cv in copies]
+            n_sus = 10 * n_copy
+            sus = []
+            for _ in range(5):
+                for ra in rot:
+                    dcall(dargs=ra)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for i in range(n_sus):
+                    dcall(dargs=rot[i % n_copy])
+                b.record(stream)
+                b.synchronize()
+                sus.append(a.elapsed_time(b) * 1e3 / n_sus)
+            us_sus = statistics.median(sus)
+            del copies, rot
             p50 = statistics.median(t)
             tps = int(ws[need - 256:need - 252].view(torch.int32).item())
             dec[dc.name] = {"us_per_call_p50": round(p50, 2), "us_p10": round(float(np.percentile(t, 10)), 2),
@@ -274,6 +301,11 @@ def main():
                             "frac_of_hbm_peak": round(nbytes / (p50 * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                             "algorithmic_bytes": nbytes, "cache_evicted": "read 1 GiB before each call",
                             "us_per_call_p50_warm": round(statistics.median(t_warm), 2),
+                            "us_per_call_sustained": round(us_sus, 2),
+                            "GB_per_s_sustained": round(nbytes / (us_sus * 1e-6) / 1e9, 1),
+                            "frac_of_hbm_peak_sustained": round(nbytes / (us_sus * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                            "sustained": f"{n_sus} calls back to back, rotating over {n_copy} copies of the cache "
+                                         f"({n_copy * cache_bytes / 2**20:.0f} MiB), median of 5 runs",
                             "B": dc.B, "Hq": dc.Hq, "Hkv": dc.Hkv, "d": dc.d, "tokens": dc.total_tokens(),
                             "paged": dc.paged, "tokens_per_split": tps,
                             "splits_per_kv_head": int(sum(-(-min(int(x), dc.max_kv_len) // tps) for x in dc.seqlens)),
@@ -490,17 +522,26 @@ def main():
         result["decode"] = dec
         traffic_dec = traffic_for("decode_split_kernel<128>@decode_long_b1h16x2kv256kd128", DECODE_KERNEL_SRC)
         long = dec["decode_long_b1h16x2kv256kd128"]
-        result["roofline_decode"] = {"bound": "hbm", "achieved": long["GB_per_s"], "peak": PEAK_HBM_GBS,
-                                     "unit": "GB/s", "frac": long["frac_of_hbm_peak"], "traffic": traffic_dec,
+        # achieved: the call's bytes over its mean duration in a timed region of
+        # back-to-back calls whose caches come from HBM (the sustained figure);
+        # the isolated call (its own event pair, caches evicted before it) is
+        # reported beside it.
+        result["roofline_decode"] = {"bound": "hbm", "achieved": long["GB_per_s_sustained"], "peak": PEAK_HBM_GBS,
+                                     "unit": "GB/s", "frac": long["frac_of_hbm_peak_sustained"], "traffic": traffic_dec,
                                      "workload": "decode_long_b1h16x2kv256kd128",
-                                     "note": "split + merge kernels per call, caches evicted (by a 1 GiB read) before each call"}
+                                     "isolated_call_GB_per_s": long["GB_per_s"],
+                                     "isolated_call_frac": long["frac_of_hbm_peak"],
+                                     "note": "split + merge kernels per call: " + long["sustained"] +
+                                             "; isolated: one call between its own event pair after a 1 GiB read"}
         long8 = dec["decode_long_b1h16x2kv256kd128_fp8"]
         result["roofline_decode_fp8"] = {
-            "bound": "hbm", "achieved": long8["GB_per_s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": long8["frac_of_hbm_peak"],
+            "bound": "hbm", "achieved": long8["GB_per_s_sustained"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": long8["frac_of_hbm_peak_sustained"],
             "traffic": traffic_for("decode_split_kernel<128, fp8>@decode_long_b1h16x2kv256kd128_fp8", DECODE_KERNEL_SRC),
             "workload": "decode_long_b1h16x2kv256kd128_fp8",
-            "note": "FP8 E4M3 cache (1 byte per element); split + merge kernels per call, caches evicted before each call"}
+            "isolated_call_GB_per_s": long8["GB_per_s"], "isolated_call_frac": long8["frac_of_hbm_peak"],
+            "note": "FP8 E4M3 cache (1 byte per element); split + merge kernels per call: " + long8["sustained"] +
+                    "; isolated: one call between its own event pair after a 1 GiB read"}
 
         result["prefill_cache"] = leg_prefill_cache()
         result["prefill_head_dims"] = leg_head_dims()
