@@ -174,8 +174,11 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillParams p) {
 // (v_mfma_f32_32x32x2_f32, full fp32 products and sums), for d = 32, 64, 96
 // and 128. One work-group of 4 waves per (128-row query tile, head, batch);
 // each wave owns 32 query rows; K and V blocks of 32 keys come into LDS by
-// direct-to-LDS loads, double-buffered, one barrier per block. (d = 128
-// holds 340 registers per lane: one wave per SIMD.)
+// direct-to-LDS loads, double-buffered, one barrier per block. Every head
+// dim fits in 256 registers with 64 KB of LDS or less, so two work-groups
+// share a CU and one's MFMAs run while the other's softmax and loads do.
+// Operand reads are a per-lane base plus a constant and are issued a few
+// MFMAs ahead of their use.
 //
 // The contraction order is permuted so that every operand comes whole from
 // 16-byte pieces: in k-step (m, e) lane half hl (lanes 32 hl .. 32 hl + 31)
@@ -188,10 +191,11 @@ __global__ void __launch_bounds__(256) prefill_f32_kernel(PrefillParams p) {
 constexpr int kKNf = 32;        // keys per block
 constexpr float kTauF = 8.0f;   // lazy rescale threshold (log2 units)
 constexpr int kXcdsF = 8;
+constexpr int kCusF = 256;     // compute units of an MI355X
 constexpr int kRsrcW3F = 0x00020000;
 
 template <int D>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D > 96 ? 1 : 2, D > 96 ? 1 : 2)))
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_f32_mfma_kernel(PrefillParams p) {
   constexpr int CH = D / 4;              // 16-byte chunks per fp32 row
   constexpr int STAGE = kKNf * D;        // floats per K or V block
@@ -207,8 +211,22 @@ prefill_f32_mfma_kernel(PrefillParams p) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ln = lane & 31;
   int t, h, b;
-  {
-    const int W = p.nT * p.Hq * p.B;
+  const int W = p.nT * p.Hq * p.B;
+  if (p.causal && W <= 2 * kCusF) {
+    // One round, two work-groups per CU: the dispatcher gives the first kCusF
+    // work-groups one CU each and the rest the second slot of the same CUs in
+    // the same order. Items ranked by cost (tile from the most keys down, then
+    // head and sequence): the first pass takes them from the top, the second
+    // from the bottom, so each CU holds a costly and a cheap tile instead of
+    // two alike.
+    const int L = blockIdx.x, F = min(W, kCusF), HB = p.Hq * p.B;
+    const int r = L < F ? L : W - 1 - (L - F);
+    t = p.nT - 1 - r / HB;
+    h = (r % HB) % p.Hq;
+    b = (r % HB) / p.Hq;
+  } else {
+    // Work item I: query tile fastest (most keys first), then head, then
+    // sequence; each XCD takes a contiguous range of items.
     const int L = blockIdx.x;
     const int xcd = L % kXcdsF, idx = L / kXcdsF;
     const int qq = W / kXcdsF, rr = W % kXcdsF;
@@ -268,6 +286,19 @@ prefill_f32_mfma_kernel(PrefillParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const int q0 = t * 128 + wave * 32;
 
+  // LDS read offsets, per lane, so that every operand read below is a base
+  // register plus a constant:
+  //   K (S^T, group m = 4a + r of 4 k-steps): row ln, 16-byte chunk
+  //   (2m + hl) ^ (ln % 8) = 8a + ((2r + hl) ^ (ln % 8)) -> kofs[r] + 128 a;
+  //   V (O^T, k-step (m, e), dim block db): row 8m + 4hl + e, dim 32 db + ln,
+  //   chunk (8 db + ln / 4) ^ (4hl + e) -> vofs[e] + 4 ((8m + e) D + 32 db).
+  int kofs[4], vofs[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    kofs[r] = ln * (D * 4) + (((2 * r + hl) ^ (ln & 7)) << 4);
+    vofs[r] = 4 * (4 * hl * D + (((ln >> 2) ^ (4 * hl + r)) << 2) + (ln & 3));
+  }
+
   if (nblk > 0) {
     dma(kbh, sK0, 0);
     dma(vbh, sV0, 0);
@@ -290,17 +321,27 @@ prefill_f32_mfma_kernel(PrefillParams p) {
     // key kv0 + 8 (r / 4) + 4 hl + r % 4
     // two accumulation chains (even and odd m), added at the end: half the
     // sequential rounding of one chain over all d products
-    // two accumulation chains (even and odd m), added at the end: half the
-    // sequential rounding of one chain over all d products
     f32x16 S = f32x16{}, S2 = f32x16{};
+    {
+      // K operands read kPFK groups ahead of their MFMAs
+      constexpr int kPFK = KM < 3 ? KM : 3;
+      auto kread = [&](int m) __attribute__((always_inline)) {
+        return *(const float4*)(kb + kofs[m & 3] + 128 * (m >> 2));
+      };
+      float4 kbuf[kPFK];
 #pragma unroll
-    for (int m = 0; m < KM; ++m) {
-      const float4 kx = *(const float4*)(kb + ln * (D * 4) + (((2 * m + hl) ^ (ln & 7)) << 4));
-      f32x16& A = (m & 1) ? S2 : S;
-      A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.x, qreg[m].x, A, 0, 0, 0);
-      A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.y, qreg[m].y, A, 0, 0, 0);
-      A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.z, qreg[m].z, A, 0, 0, 0);
-      A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.w, qreg[m].w, A, 0, 0, 0);
+      for (int i = 0; i < kPFK; ++i) kbuf[i] = kread(i);
+#pragma unroll
+      for (int m = 0; m < KM; ++m) {
+        const float4 kx = kbuf[m % kPFK];
+        if (m + kPFK < KM) kbuf[m % kPFK] = kread(m + kPFK);
+        f32x16& A = (m & 1) ? S2 : S;
+        A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.x, qreg[m].x, A, 0, 0, 0);
+        A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.y, qreg[m].y, A, 0, 0, 0);
+        A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.z, qreg[m].z, A, 0, 0, 0);
+        A = __builtin_amdgcn_mfma_f32_32x32x2f32(kx.w, qreg[m].w, A, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) S[r] += S2[r];
@@ -341,20 +382,28 @@ prefill_f32_mfma_kernel(PrefillParams p) {
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
     // O^T += V^T . P^T: k-step (m, e) contracts key 8m + 4hl + e, whose
-    // probability is this lane's register 4m + e
+    // probability is this lane's register 4m + e. MFMA n of the stream is
+    // (m, e, db) = (n / (4 DB), (n / DB) % 4, n % DB); its V^T operand is read
+    // kPFV MFMAs ahead.
+    {
+      constexpr int kNV = 16 * DB;
+      constexpr int kPFV = 8;
+      const char* vbb = (const char*)vb;
+      auto vread = [&](int n) __attribute__((always_inline)) {
+        const int m = n / (4 * DB), e = (n / DB) & 3, db = n % DB;
+        return *(const float*)(vbb + vofs[e] + 4 * ((8 * m + e) * D + 32 * db));
+      };
+      float vbuf[kPFV];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+      for (int i = 0; i < kPFV; ++i) vbuf[i] = vread(i);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 8 * m + 4 * hl + e;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const int dim = 32 * db + ln;
-          const float vx = vb[row * D + ((((dim >> 2) ^ (row & 7))) << 2) + (dim & 3)];
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vx, S[4 * m + e], O[db], 0, 0, 0);
-        }
+      for (int n = 0; n < kNV; ++n) {
+        const float vx = vbuf[n % kPFV];
+        if (n + kPFV < kNV) vbuf[n % kPFV] = vread(n + kPFV);
+        const int m = n / (4 * DB), e = (n / DB) & 3, db = n % DB;
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x2f32(vx, S[4 * m + e], O[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-
     }
   }
 
