@@ -59,6 +59,21 @@ struct HdCfg {
 
 // K rows are read 16 bytes per lane for 32 consecutive rows at one chunk:
 // XOR with row mod RP spreads 8 consecutive rows over 8 distinct chunks.
+// At d > 128 a wave holds O^T (128 registers) and Q^T (64) and needs more
+// than 256 registers. Q^T is only ever an MFMA operand, so it is kept in the
+// accumulation registers (the empty asm pins it there at the top of each
+// block) and O^T stays in the vector registers, where the rare rescale and
+// the epilogue use it; this file is compiled with the MFMA results in vector
+// registers (-mllvm -amdgpu-mfma-vgpr-form=1, set by the build). Otherwise
+// O^T is copied between the two register files on every block.
+template <int D>
+__device__ __forceinline__ void pin_q(bf16x8* qreg) {
+  if constexpr (D > 128) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) asm volatile("" : "+a"(qreg[ks]));
+  }
+}
+
 template <int D>
 __device__ __forceinline__ int hswz_k(int row) { return row & (HdCfg<D>::RP - 1); }
 // V^T transpose reads: each 16-lane group reads 4 consecutive rows x 32
@@ -253,6 +268,7 @@ prefill_hd_kernel(PrefillParams p) {
   }
   const int q0 = t * kTile + wave * 32;
   for (int j = 0; j < nblk; ++j) {
+    pin_q<D>(qreg);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block j
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
     __syncthreads();
@@ -268,10 +284,25 @@ prefill_hd_kernel(PrefillParams p) {
     const char* vb = (const char*)(odd ? sV1 : sV0);
 
     f32x16 S0 = f32x16{}, S1 = f32x16{};
+    {
+      // K operands read kPFS MFMAs ahead (MFMA n: k-step n / 2, sub-tile n % 2)
+      constexpr int kNS = 2 * C::KS, kPFS = 4;
+      auto kop = [&](int n) __attribute__((always_inline)) {
+        return (n & 1) ? kread(kb, kr1, sw1, n >> 1) : kread(kb, kr0, sw0, n >> 1);
+      };
+      bf16x8 kbuf[kPFS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks) {
-      S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kb, kr0, sw0, ks), qreg[ks], S0, 0, 0, 0);
-      S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(kb, kr1, sw1, ks), qreg[ks], S1, 0, 0, 0);
+      for (int n = 0; n < kPFS; ++n) kbuf[n] = kop(n);
+#pragma unroll
+      for (int n = 0; n < kNS; ++n) {
+        const bf16x8 a = kbuf[n % kPFS];
+        if (n + kPFS < kNS) kbuf[n % kPFS] = kop(n + kPFS);
+        if (n & 1)
+          S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[n >> 1], S1, 0, 0, 0);
+        else
+          S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[n >> 1], S0, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // key of register r of sub-tile u is kv0 + 32u + 4hl + 8(r/4) + r%4;
     // visible iff < Skv and (non-causal or) <= query row + off
@@ -525,6 +556,7 @@ prefill_hd_ks_kernel(PrefillParams p) {
     dma(vbh, sV[0][kh], voff, kh);
   }
   for (int i = 0; i < iters; ++i) {
+    pin_q<D>(qreg);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of its block
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
     __syncthreads();
@@ -540,10 +572,23 @@ prefill_hd_ks_kernel(PrefillParams p) {
     const char* kb = (const char*)sK[st][kh];
     const char* vb = (const char*)sV[st][kh];
     f32x16 S = f32x16{};
+    {
+      // K operands read kPFS k-steps ahead
+      constexpr int kPFS = C::KS < 4 ? C::KS : 4;
+      auto kop = [&](int ks) __attribute__((always_inline)) {
+        return *(const bf16x8*)(kb + kr0 + (((2 * ks + hl) ^ sw0) << 4));
+      };
+      bf16x8 kbuf[kPFS];
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*(const bf16x8*)(kb + kr0 + (((2 * ks + hl) ^ sw0) << 4)),
-                                                 qreg[ks], S, 0, 0, 0);
+      for (int n = 0; n < kPFS; ++n) kbuf[n] = kop(n);
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+        const bf16x8 a = kbuf[ks % kPFS];
+        if (ks + kPFS < C::KS) kbuf[ks % kPFS] = kop(ks + kPFS);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qreg[ks], S, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     // key of register r is kv0 + 4hl + 8(r/4) + r%4
     const bool full = kv0 + kKBKs <= Skv && (!causal || kv0 + kKBKs - 1 <= q0 + off);
     if (!full) {

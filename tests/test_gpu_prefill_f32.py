@@ -33,6 +33,10 @@ SHAPES = [
     (2, 32, 32, 300, 2000, 128, True),   # Sq < Skv, bottom-right causal
     (1, 32, 4, 1500, 383, 128, False),   # MQA-like, Sq > Skv
     (3, 16, 8, 383, 1031, 64, True),
+    # causal grids of one round at two work-groups per CU (256 < tiles <= 512:
+    # costly and cheap tiles paired per CU), with Sq < Skv and a ragged last tile
+    (3, 16, 8, 900, 1200, 64, True),
+    (1, 48, 16, 1000, 1000, 128, True),
 ]
 
 
