@@ -430,11 +430,12 @@ prefill_f32_mfma_kernel(PrefillParams p) {
 }  // namespace
 
 hipError_t launch_prefill_f32(const PrefillParams& p, int d, hipStream_t stream) {
-  // Grids of at least 128 query tiles of 128 rows (over heads and batch) take
+  // Grids of at least 64 query tiles of 128 rows (over heads and batch) take
   // the matrix-core kernel (d <= 128); smaller ones, bound by launch latency
   // or by too few work-groups for the CUs, take the vector kernel, whose
-  // work-groups own 4 rows each.
-  if (d <= 128 && (long)p.nT * p.Hq * p.B >= 128) {
+  // work-groups own 4 rows each (measured: the vector kernel is faster up to
+  // 32 tiles, the two are even near 48, the matrix cores faster from 64).
+  if (d <= 128 && (long)p.nT * p.Hq * p.B >= 64) {
     const dim3 grid(p.nT * p.Hq * p.B), block(256);
     if (d == 128)
       return launch_kernel(prefill_f32_mfma_kernel<128>, grid, block, stream, p);

@@ -108,7 +108,7 @@ fa_status fa_prefill(const void* q, const void* k, const void* v, void* o,
 /*
  * fa_prefill_f32 - the same operation with fp32 q, k, v, o and fp32 arithmetic
  * throughout (no bf16 rounding anywhere). Same arguments and layouts as
- * fa_prefill; d is 32, 64, 96, 128 or 256. Grids of at least 128 query tiles
+ * fa_prefill; d is 32, 64, 96, 128 or 256. Grids of at least 64 query tiles
  * of 128 rows (over heads and batch) at d <= 128 run on the fp32 matrix cores
  * (full fp32 products and sums); smaller ones on fp32 vector FMA.
  */

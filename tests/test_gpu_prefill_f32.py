@@ -1,5 +1,5 @@
 """GPU parity of fa_prefill_f32 on grids large enough for its matrix-core
-kernel (v_mfma_f32_32x32x2_f32, at least 128 query tiles of 128 rows over
+kernel (v_mfma_f32_32x32x2_f32, at least 64 query tiles of 128 rows over
 heads and batch; d = 32, 64, 96, 128), every output element against the fp64
 oracle to the fp32 bound. Smaller shapes (the vector kernel) are covered in
 test_gpu_prefill.py and test_gpu_prefill_hd.py.
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 def run_and_check(case):
     torch_gpu()
-    assert -(-case.Sq // 128) * case.Hq * case.B >= 128  # the matrix-core kernel
+    assert -(-case.Sq // 128) * case.Hq * case.B >= 64  # the matrix-core kernel
     print(f"case {case.name} scale={case.scale:.4g}", flush=True)
     o = fa.prefill(dev_f32(case.q), dev_f32(case.k), dev_f32(case.v), causal=case.causal, scale=case.scale)
     q, k, v = case.as_f64()
@@ -37,6 +37,9 @@ SHAPES = [
     # costly and cheap tiles paired per CU), with Sq < Skv and a ragged last tile
     (3, 16, 8, 900, 1200, 64, True),
     (1, 48, 16, 1000, 1000, 128, True),
+    # the smallest grids on the matrix cores (64 tiles)
+    (1, 8, 8, 1024, 1024, 64, True),
+    (1, 4, 2, 2048, 2048, 128, False),
 ]
 
 
