@@ -559,7 +559,11 @@ prefill_hd_ks_kernel(PrefillParams p) {
     pin_q<D>(qreg);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of its block
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
-    __syncthreads();
+    // With one row part (RH = 1) each wave loads and reads only its own key
+    // part's stages, so its own waits above order everything and the key
+    // parts run their chains without meeting; waves that share a block (RH =
+    // 2) meet here.
+    if constexpr (RH > 1) __syncthreads();
     const int st = i & 1;
     const int jn = KH * (i + 1) + kh;
     if (jn < nb) {
