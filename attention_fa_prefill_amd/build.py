@@ -78,6 +78,7 @@ def _build_one(sources, lib, verbose):
         for proc in procs:
             if proc.poll() is None:
                 proc.kill()
+                proc.communicate()
         for obj in objs:
             if os.path.exists(obj):
                 os.remove(obj)
