@@ -360,13 +360,24 @@ prefill_hd_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
+    {
+      // V^T operands read kPFV MFMAs ahead (MFMA n: sub n / (2 DB), s (n / DB) % 2, db n % DB)
+      constexpr int kNV = 4 * C::DB, kPFV = 4;
+      auto vop = [&](int n) __attribute__((always_inline)) {
+        return vread(vb, n / (2 * C::DB), (n / C::DB) & 1, n % C::DB);
+      };
+      bf16x8 vbuf[kPFV];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+      for (int n = 0; n < kPFV; ++n) vbuf[n] = vop(n);
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-          O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vb, sub, s, db), P[sub][s], O[db], 0, 0, 0);
+      for (int n = 0; n < kNV; ++n) {
+        const bf16x8 a = vbuf[n % kPFV];
+        if (n + kPFV < kNV) vbuf[n % kPFV] = vop(n + kPFV);
+        const int db = n % C::DB;
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[n / (2 * C::DB)][(n / C::DB) & 1], O[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
 
   // normalise and store (rows past Sq are not written; CACHE: a row with no
@@ -656,11 +667,21 @@ prefill_hd_ks_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
+    {
+      // V^T operands read kPFV MFMAs ahead (MFMA n: s n / DB, db n % DB)
+      constexpr int kNV = 2 * C::DB, kPFV = kNV < 4 ? kNV : 4;
+      bf16x8 vbuf[kPFV];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+      for (int n = 0; n < kPFV; ++n) vbuf[n] = vread(vb, n / C::DB, n % C::DB);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread(vb, s, db), P[s], O[db], 0, 0, 0);
+      for (int n = 0; n < kNV; ++n) {
+        const bf16x8 a = vbuf[n % kPFV];
+        if (n + kPFV < kNV) vbuf[n % kPFV] = vread(vb, (n + kPFV) / C::DB, (n + kPFV) % C::DB);
+        const int db = n % C::DB;
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, P[n / C::DB], O[db], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   }
 
   // merge the key parts: the kh > 0 waves hand (m, l, O) to the kh = 0 wave
@@ -750,9 +771,11 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
     else
       return hipErrorInvalidValue;
   }
-  // d = 32, and d = 256 grids of fewer than two rounds of 128-row tiles (one
-  // work-group per CU), take the key-split kernel, whose 64-row tiles
-  // balance the CUs
+  // d = 32 takes the key-split kernel; d = 256 takes it on causal grids of
+  // fewer than two rounds of 128-row tiles (one work-group per CU) with at
+  // least 10 tiles per head, where the one-group kernel's longest tile would
+  // set the time (measured: key-split faster from 12 tiles per head, the
+  // one-group kernel from 8 tiles down and on every non-causal grid)
   const long tiles64 = (long)((p.Sq + 63) / 64) * p.Hq * p.B;
   const dim3 grid_ks2(tiles64), grid_ks4(((p.Sq + 31) / 32) * p.Hq * p.B);
   // d = 32: four key parts on causal grids of at most two rounds of 64-row
@@ -761,7 +784,7 @@ hipError_t launch_prefill_hd(const PrefillParams& p, int d, hipStream_t stream) 
     return launch_kernel(prefill_hd_ks_kernel<32, 4, false>, grid_ks4, block, stream, p);
   else if (d == 32)
     return launch_kernel(prefill_hd_ks_kernel<32, 2, false>, grid_ks2, block, stream, p);
-  else if (d == 256 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
+  else if (d == 256 && p.causal && p.nT >= 10 && p.cus > 0 && (long)p.nT * p.Hq * p.B < 2L * p.cus)
     return launch_kernel(prefill_hd_ks_kernel<256, 2, false>, grid_ks2, block, stream, p);
   else if (d == 256)
     return launch_kernel(prefill_hd_kernel<256, false>, grid, block, stream, p);

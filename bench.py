@@ -359,15 +359,17 @@ def main():
         n_cus = torch.cuda.get_device_properties(0).multi_processor_count
 
         def hd_kernel_name(hc):
-            # d = 32, and d = 256 grids under two rounds of 128-row tiles, take the key-split kernel
-            # (d = 32: four key parts on causal grids of at most 8 * CUs 64-row tiles, else two)
+            # d = 32 takes the key-split kernel (four key parts on causal grids of at most 8 * CUs
+            # 64-row tiles, else two); d = 256 takes it on causal grids under two rounds of 128-row
+            # tiles with at least 10 tiles per head
             tiles = -(-hc.Sq // 128) * hc.Hq * hc.B
             if hc.d == 96:
                 return "prefill_bf16_kernel<96, false>"
             if hc.d == 32:
                 return "prefill_hd_ks_kernel<32, 4, false>" if -(-hc.Sq // 64) * hc.Hq * hc.B <= 8 * n_cus else \
                     "prefill_hd_ks_kernel<32, 2, false>"
-            return ("prefill_hd_ks_kernel<256, 2, false>" if hc.d == 256 and tiles < 2 * n_cus
+            return ("prefill_hd_ks_kernel<256, 2, false>"
+                    if hc.d == 256 and hc.causal and -(-hc.Sq // 128) >= 10 and tiles < 2 * n_cus
                     else f"prefill_hd_kernel<{hc.d}, false>")
         hd = {}
         for hc in (workloads.prefill_gqa_d256(), workloads.prefill_mha_d96(), workloads.prefill_gqa_d32()):
