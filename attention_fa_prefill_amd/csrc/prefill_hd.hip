@@ -432,6 +432,11 @@ __device__ __forceinline__ int ks_swz_k(int row) { return D <= 32 ? (row >> 2) &
 template <int D>
 __device__ __forceinline__ int ks_swz_v(int row) { return D <= 32 ? 0 : hswz_v<D>(row); }
 
+template <int N>
+struct StageIdx {
+  static constexpr int value = N;
+};
+
 template <int D, int KH_, bool CACHE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HdCfg<D>::OCC, HdCfg<D>::OCC)))
 prefill_hd_ks_kernel(PrefillParams p) {
@@ -440,11 +445,16 @@ prefill_hd_ks_kernel(PrefillParams p) {
   static_assert(KH_ == 2 || KH_ == 4, "two or four key parts");
   constexpr int KH = K::KH, RH = K::RH, RP = K::RP, STG = K::STG, NIK = K::NIK;
   static_assert(NIK >= 1 && 64 * NIK * RH == kKBKs * RP, "a block's chunks are split evenly between its waves");
-  static_assert((KH - 1) * C::DB * 4 * 64 * RH * 16 <= 2 * KH * STG * 2, "the merge's partial outputs fit in sK");
-  static_assert((KH - 1) * 128 * RH * 4 <= 2 * KH * STG * 2, "the merge's (m, l) fit in sV");
-  // [stage][key part]; the merge reuses this memory
-  __shared__ __attribute__((aligned(1024))) __bf16 sK[2][KH][STG];
-  __shared__ __attribute__((aligned(1024))) __bf16 sV[2][KH][STG];
+  static_assert((KH - 1) * C::DB * 4 * 64 * RH * 16 <= 2 * KH * STG * 2, "the merge's partial outputs fit in sK0, sK1");
+  static_assert((KH - 1) * 128 * RH * 4 <= KH * STG * 2, "the merge's (m, l) fit in sV0");
+  // One array per stage ([key part]), and the loop below names the stages at
+  // compile time: the compiler then tells a block's operand reads from the
+  // direct-to-LDS loads still in flight into the other stage, and does not
+  // make the reads wait for them. The merge reuses this memory.
+  __shared__ __attribute__((aligned(1024))) __bf16 sK0[KH][STG];
+  __shared__ __attribute__((aligned(1024))) __bf16 sK1[KH][STG];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV0[KH][STG];
+  __shared__ __attribute__((aligned(1024))) __bf16 sV1[KH][STG];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -454,7 +464,7 @@ prefill_hd_ks_kernel(PrefillParams p) {
   const int nT = (p.Sq + K::TILE - 1) / K::TILE;
   int t, h, b;
   if constexpr (CACHE) {
-    if (!ranked_cache_item(p, nT, tid, (int*)&sK[0][0][0], b, h, t)) return;
+    if (!ranked_cache_item(p, nT, tid, (int*)&sK0[0][0], b, h, t)) return;
   } else {
     const int W = nT * p.Hq * p.B;
     const int L = blockIdx.x;
@@ -563,10 +573,15 @@ prefill_hd_ks_kernel(PrefillParams p) {
   };
 
   if (kh < nb) {
-    dma(kbh, sK[0][kh], koff, kh);
-    dma(vbh, sV[0][kh], voff, kh);
+    dma(kbh, sK0[kh], koff, kh);
+    dma(vbh, sV0[kh], voff, kh);
   }
-  for (int i = 0; i < iters; ++i) {
+  auto step = [&](auto stage, int i) __attribute__((always_inline)) {
+    constexpr int st = decltype(stage)::value;
+    auto& kcur = st ? sK1 : sK0;
+    auto& vcur = st ? sV1 : sV0;
+    auto& knxt = st ? sK0 : sK1;
+    auto& vnxt = st ? sV0 : sV1;
     pin_q<D>(qreg);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of its block
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
@@ -575,17 +590,30 @@ prefill_hd_ks_kernel(PrefillParams p) {
     // parts run their chains without meeting; waves that share a block (RH =
     // 2) meet here.
     if constexpr (RH > 1) __syncthreads();
-    const int st = i & 1;
     const int jn = KH * (i + 1) + kh;
-    if (jn < nb) {
-      dma(kbh, sK[st ^ 1][kh], koff, jn);
-      dma(vbh, sV[st ^ 1][kh], voff, jn);
-    }
     const int jb = KH * i + kh;
     const int kv0 = jb * kKBKs;
-    if (jb >= nb || (causal && kv0 > q0 + 31 + off)) continue;
-    const char* kb = (const char*)sK[st][kh];
-    const char* vb = (const char*)sV[st][kh];
+    const bool live = !(jb >= nb || (causal && kv0 > q0 + 31 + off));
+    const char* kb = (const char*)kcur[kh];
+    const char* vb = (const char*)vcur[kh];
+    // The compiler cannot tell a V^T transpose read from the loads in flight
+    // into the other stage and would make it wait for them: at d = 32 the
+    // block's V^T operands (8 registers) are therefore read before the next
+    // block's loads are issued.
+    constexpr int kNV = 2 * C::DB;
+    constexpr bool kVFirst = D <= 32;
+    bf16x8 vpre[kVFirst ? kNV : 1];
+    if constexpr (kVFirst) {
+      if (live) {
+#pragma unroll
+        for (int n = 0; n < kNV; ++n) vpre[n] = vread(vb, n / C::DB, n % C::DB);
+      }
+    }
+    if (jn < nb) {
+      dma(kbh, knxt[kh], koff, jn);
+      dma(vbh, vnxt[kh], voff, jn);
+    }
+    if (!live) return;
     f32x16 S = f32x16{};
     {
       // K operands read kPFS k-steps ahead
@@ -667,9 +695,15 @@ prefill_hd_ks_kernel(PrefillParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) O[db][r] *= alpha;
     }
-    {
+    if constexpr (kVFirst) {
+#pragma unroll
+      for (int n = 0; n < kNV; ++n) {
+        const int db = n % C::DB;
+        O[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vpre[n], P[n / C::DB], O[db], 0, 0, 0);
+      }
+    } else {
       // V^T operands read kPFV MFMAs ahead (MFMA n: s n / DB, db n % DB)
-      constexpr int kNV = 2 * C::DB, kPFV = kNV < 4 ? kNV : 4;
+      constexpr int kPFV = kNV < 4 ? kNV : 4;
       bf16x8 vbuf[kPFV];
 #pragma unroll
       for (int n = 0; n < kPFV; ++n) vbuf[n] = vread(vb, n / C::DB, n % C::DB);
@@ -682,22 +716,32 @@ prefill_hd_ks_kernel(PrefillParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  for (int i = 0; i < iters; i += 2) {
+    step(StageIdx<0>{}, i);
+    if (i + 1 < iters) step(StageIdx<1>{}, i + 1);
   }
 
   // merge the key parts: the kh > 0 waves hand (m, l, O) to the kh = 0 wave
   // of the same rows through LDS (the stages are free once every wave is here)
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  float4* xo = (float4*)&sK[0][0][0];  // [key part - 1][row part][db][rg][lane]
-  float* xm = (float*)&sV[0][0][0];    // [key part - 1][row part][m, l][lane]
+  // O: [key part - 1][row part][db][rg][lane] in float4s over sK0, then sK1
+  // (KX float4s each, a multiple of 64, so a wave's 64 never straddle them)
+  constexpr int KX = KH * STG / 8;
+  static_assert(KX % 64 == 0, "a wave's float4s lie in one array");
+  auto xo = [&](int f) __attribute__((always_inline)) {
+    return f < KX ? (float4*)&sK0[0][0] + f : (float4*)&sK1[0][0] + (f - KX);
+  };
+  float* xm = (float*)&sV0[0][0];  // [key part - 1][row part][m, l][lane]
   constexpr int XO = RH * C::DB * 4 * 64, XM = RH * 128;
   if (kh > 0) {
-    float4* xw = xo + (kh - 1) * XO + rh * (C::DB * 4 * 64);
+    const int xw = (kh - 1) * XO + rh * (C::DB * 4 * 64);
 #pragma unroll
     for (int db = 0; db < C::DB; ++db)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg)
-        xw[(db * 4 + rg) * 64 + lane] =
+        *xo(xw + (db * 4 + rg) * 64 + lane) =
             make_float4(O[db][4 * rg], O[db][4 * rg + 1], O[db][4 * rg + 2], O[db][4 * rg + 3]);
     float* xmw = xm + (kh - 1) * XM + rh * 128;
     xmw[lane] = m_run;
@@ -735,7 +779,7 @@ prefill_hd_ks_kernel(PrefillParams p) {
           float v2 = O[db][4 * rg + 2] * f[0], v3 = O[db][4 * rg + 3] * f[0];
 #pragma unroll
           for (int u = 1; u < KH; ++u) {
-            const float4 o1 = xo[(u - 1) * XO + rh * (C::DB * 4 * 64) + (db * 4 + rg) * 64 + lane];
+            const float4 o1 = *xo((u - 1) * XO + rh * (C::DB * 4 * 64) + (db * 4 + rg) * 64 + lane);
             v0 += o1.x * f[u];
             v1 += o1.y * f[u];
             v2 += o1.z * f[u];
