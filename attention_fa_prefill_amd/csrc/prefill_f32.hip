@@ -194,6 +194,11 @@ constexpr int kXcdsF = 8;
 constexpr int kCusF = 256;     // compute units of an MI355X
 constexpr int kRsrcW3F = 0x00020000;
 
+template <int N>
+struct StageF {
+  static constexpr int value = N;
+};
+
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_f32_mfma_kernel(PrefillParams p) {
@@ -303,17 +308,20 @@ prefill_f32_mfma_kernel(PrefillParams p) {
     dma(kbh, sK0, 0);
     dma(vbh, sV0, 0);
   }
-  for (int j = 0; j < nblk; ++j) {
+  // The loop runs two blocks per iteration with the stages named at compile
+  // time, so the compiler tells a block's operand reads from the loads still
+  // in flight into the other stage and does not make the reads wait for them.
+  auto step = [&](auto stage, int j) __attribute__((always_inline)) {
+    constexpr bool odd = decltype(stage)::value != 0;
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of block j
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): reads of the other stage are done
     __syncthreads();
-    const bool odd = j & 1;
     if (j + 1 < nblk) {
       dma(kbh, odd ? sK0 : sK1, j + 1);
       dma(vbh, odd ? sV0 : sV1, j + 1);
     }
     const int kv0 = j * kKNf;
-    if (causal && kv0 > q0 + 31 + off) continue;  // above every row of this wave
+    if (causal && kv0 > q0 + 31 + off) return;  // above every row of this wave
     const char* kb = (const char*)(odd ? sK1 : sK0);
     const float* vb = odd ? sV1 : sV0;
 
@@ -405,6 +413,10 @@ prefill_f32_mfma_kernel(PrefillParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+  };
+  for (int j = 0; j < nblk; j += 2) {
+    step(StageF<0>{}, j);
+    if (j + 1 < nblk) step(StageF<1>{}, j + 1);
   }
 
   // normalise and store: lane (query ln, half hl) register r of O[db] holds
